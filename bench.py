@@ -1,0 +1,191 @@
+"""Throughput of the exact row-wise Top-K selector on one MI355X.
+
+One step is one topk_filtered call over one batch of synthetic score rows
+(every phase of the selector runs inside it).  Inputs are resident in HBM
+before timing starts.  Calls are captured in a HIP graph over R rotated copies
+of the batch (R chosen so the copies span at least twice the 256 MB
+last-level cache, so replays stream from HBM), then replayed.  The timed
+region is exactly --steps calls, bracketed by device synchronisation, timed
+with HIP events on the stream the graph runs on.
+
+Prints one JSON line: effective score-row GB/s (sum over rows of 4*ke bytes per
+second) with rows/s, the roofline of the selector kernel and the CPU oracle's
+rate on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+DESCRIPTIONS = {
+    "tiny": "tiny: M=4, N=8192, ke=[8192,6000,3000,1024], K=256, iid N(0,1)",
+    "decode": "decode indexer: M=64, N=131072, ke~U[32768,131072], K=2048, "
+              "8-head ReLU-weighted scores",
+    "prefill": "causal prefill: M=4096, N=65536, ke=min(61440+r+1,N), K=2048, "
+               "8-head ReLU-weighted scores",
+    "long": "few long rows: M=4, N=524288, ke=N, K=2048, ReLU scores + 0.1% +3sigma spikes",
+    "adversarial": "adversarial: M=256, N=262144, ke~U[4096,N], K=2048, ties/sorted/"
+                   "constant/+-inf rows",
+}
+
+
+def algorithmic_bytes(ke, n: int, k: int, stride: int) -> int:
+    """Bytes the selector must move per call: one complete read of every valid
+    row, the 1/s view, and the K int32 outputs per row."""
+    total = 0
+    for L in ke:
+        L = min(max(int(L), 0), n)
+        if L > k:
+            view = math.ceil(L / stride) if stride else 0
+            total += 4 * L + 4 * view
+        total += 4 * k
+    return total
+
+
+def cpu_baseline(w, seconds: float) -> dict:
+    """The CPU oracle (complete sort per row, threaded over rows) on the same batch."""
+    from oracle import oracle
+    threads = oracle.default_threads()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.topk(w.x, w.ke, w.k, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    per_call = el / reps
+    return {"value": round(w.score_bytes() / per_call / 1e9, 4), "unit": "GB/s",
+            "rows_per_s": round(w.m / per_call, 1), "cores": threads, "kind": "oracle",
+            "sample": "whole %s batch (%d rows) x %d repetitions, %.1f s wall" % (
+                w.name, w.m, reps, el)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--config", default="decode", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the selector has no multi-GPU path "
+              "(rows are independent; see the sharding note in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from exact_row_wise_sampled_amd import topkf, workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.make(args.config)
+    m, n, k = w.m, w.n, w.k
+    plan = topkf.plan_for(m, n, torch.cuda.get_device_properties(dev).multi_processor_count)
+    x_bytes = m * n * 4
+    copies = max(2, math.ceil(2 * MALL_BYTES / x_bytes))
+    base = torch.from_numpy(w.x).to(dev)
+    xs = [base] + [base.clone() for _ in range(copies - 1)]
+    ke = torch.from_numpy(w.ke).to(dev)
+    nvr = torch.tensor([m], dtype=torch.int32, device=dev)
+    outs = [torch.empty((m, k), dtype=torch.int32, device=dev) for _ in range(copies)]
+    sel = topkf.Selector(m, n, device=dev)
+    torch.cuda.synchronize()
+
+    if not args.no_check:
+        from oracle import oracle
+        sel(xs[-1], ke, outs[-1], nvr, k)
+        torch.cuda.synchronize()
+        res = oracle.topk(w.x, w.ke, k)
+        fails = oracle.check_rows(outs[-1].cpu().numpy(), w.x, res)
+        if fails:
+            print("bench: output differs from the oracle: %s" % fails, file=sys.stderr)
+            return 1
+        print("bench: %s output matches the oracle (%d rows)" % (w.name, m), file=sys.stderr,
+              flush=True)
+
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in range(copies):
+            sel(xs[i], ke, outs[i], nvr, k, stream=stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(copies):
+            sel(xs[i], ke, outs[i], nvr, k, stream=stream)
+    torch.cuda.synchronize()
+
+    reps_warm = max(1, math.ceil(args.warmup / copies))
+    reps = max(1, math.ceil(args.steps / copies))
+    steps = reps * copies
+    with torch.cuda.stream(stream):
+        for _ in range(reps_warm):
+            graph.replay()
+    torch.cuda.synchronize()
+    if int(sel.counters.sum().item()) != 0:
+        print("bench: counters not zero after replays", file=sys.stderr)
+        return 1
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / steps
+
+    score_bytes = w.score_bytes()
+    gbs = score_bytes / (ms_step * 1e-3) / 1e9
+    alg = algorithmic_bytes(w.ke, n, k, plan.stride)
+    achieved = alg / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": "score-row GB/s and rows/s vs HBM peak, K=2048, ragged rows up to 512K",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "rows_per_s": round(m / (ms_step * 1e-3), 1),
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_warm * copies,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS[args.config], "M": m, "N": n, "K": k,
+                   "score_bytes": score_bytes, "rotated_copies": copies,
+                   "plan": plan.as_dict()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": alg,
+                     "kernel": "persistent_kernel" if plan.family == 1 else "kvsplit_kernel"},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

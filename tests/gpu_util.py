@@ -1,0 +1,65 @@
+"""Shared helpers of the GPU tests: run the HIP selector through the C ABI on
+host-generated inputs and compare with the CPU oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from oracle import oracle
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def note(msg: str) -> None:
+    """Names the case about to run on the GPU (flushed, so it survives a crash)."""
+    print("[gpu] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_topk(x: np.ndarray, ke: np.ndarray, k: int, m_live: int | None = None, plan=None,
+             stats: bool = False, x_dev=None, canary: int = -7, stride_pad: int = 0):
+    """Runs topk_filtered (or the debug entry with `plan`) and returns (out, stats, sel).
+
+    stride_pad > 0 stores the rows at a pitch of N + stride_pad elements.
+    """
+    import torch
+    from exact_row_wise_sampled_amd import topkf
+    d = dev()
+    m, n = x.shape
+    if x_dev is None:
+        if stride_pad:
+            buf = torch.empty((m, n + stride_pad), dtype=torch.float32, device=d)
+            buf[:, :n] = torch.from_numpy(x).to(d)
+            buf[:, n:] = float("nan")
+            x_dev = buf[:, :n]
+        else:
+            x_dev = torch.from_numpy(np.ascontiguousarray(x)).to(d)
+    ke_d = torch.from_numpy(np.ascontiguousarray(ke, dtype=np.int32)).to(d)
+    out = torch.full((m, k), canary, dtype=torch.int32, device=d)
+    nvr = torch.tensor([m if m_live is None else m_live], dtype=torch.int32, device=d)
+    sel = topkf.Selector(m, n, device=d, plan=plan)
+    rs = torch.zeros(topkf.ROUTE_COUNT, dtype=torch.int32, device=d) if (stats or plan) else None
+    sel(x_dev, ke_d, out, nvr, k, route_stats=rs)
+    torch.cuda.synchronize()
+    counters_zero = int(sel.counters.sum().item()) == 0
+    assert counters_zero, "counters not returned to zero"
+    st = None
+    if rs is not None:
+        st = dict(zip(topkf.ROUTE_NAMES, rs.cpu().numpy().tolist()))
+    return out.cpu().numpy(), st, sel
+
+
+def assert_exact(out: np.ndarray, x: np.ndarray, ke: np.ndarray, k: int, m_live=None,
+                 res=None, canary: int = -7) -> None:
+    m = x.shape[0]
+    if res is None:
+        res = oracle.topk(x, ke, k, m_live=m_live)
+    fails = oracle.check_rows(out, x, res)
+    assert not fails, "\n".join(fails)
+    # rows at or beyond M_live are untouched
+    if res.rows < m:
+        assert (out[res.rows:] == canary).all(), "rows >= M_live were written"

@@ -1,0 +1,99 @@
+"""Host-side checks of the C ABI library: it loads, exports what include/topkf.h
+declares, and its host-only planner behaves.  No GPU compute is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topkf.h")
+LIB = os.path.join(ROOT, "exact_row_wise_sampled_amd", "libtopkf.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s+\*?\s*([A-Za-z_]\w*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libtopkf.so is not built; run __graft_entry__.build()")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for want in ("topk_filtered_workspace_size", "topk_filtered", "topkf_status_string",
+                 "topkf_plan_for", "topkf_plan_workspace_size", "topk_filtered_debug",
+                 "topkf_coarse_keys"):
+        assert want in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True,
+                         text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings():
+    from exact_row_wise_sampled_amd import topkf
+    assert topkf.status_string(0) == "ok"
+    assert "workspace" in topkf.status_string(3)
+    assert topkf.status_string(99) == "unknown status"
+
+
+def test_planner_maps_workload_shapes():
+    from exact_row_wise_sampled_amd import topkf
+    cus = 256
+    tiny = topkf.plan_for(4, 8192, cus)
+    assert tiny.family == topkf.FAMILY_PERSISTENT and tiny.stride == 0 and tiny.workers == 4
+    prefill = topkf.plan_for(4096, 65536, cus)
+    assert prefill.family == topkf.FAMILY_PERSISTENT and prefill.stride == 128
+    assert prefill.workers == 2 * cus and prefill.dual == 1
+    decode = topkf.plan_for(64, 131072, cus)
+    assert decode.family == topkf.FAMILY_KVSPLIT and decode.stride == 128
+    assert decode.splits * 64 >= 2 * cus
+    long_ = topkf.plan_for(4, 524288, cus)
+    assert long_.family == topkf.FAMILY_KVSPLIT
+    assert long_.splits <= 524288 // long_.min_segment
+    mid = topkf.plan_for(1024, 32768, cus)
+    assert mid.stride == 64
+
+
+def test_planner_is_deterministic_and_validates():
+    from exact_row_wise_sampled_amd import topkf
+    a = topkf.plan_for(300, 200000, 256).as_dict()
+    b = topkf.plan_for(300, 200000, 256).as_dict()
+    assert a == b
+    with pytest.raises(topkf.TopkfError):
+        topkf.plan_for(-1, 100, 256)
+    with pytest.raises(topkf.TopkfError):
+        topkf.plan_for(10, 0, 256)
+    with pytest.raises(topkf.TopkfError):
+        topkf.plan_for(10, 100, 0)
+
+
+def test_workspace_sizes_follow_the_plan():
+    from exact_row_wise_sampled_amd import topkf
+    n = 100000
+    pers = topkf.make_plan(topkf.FAMILY_PERSISTENT, 128, 1, workers=10)
+    cb, wb = topkf.plan_workspace_size(pers, 77, n)
+    assert cb == 4 * (64 + 2 * 77)
+    assert wb == 10 * 2 * n * 8          # two (index, key) spill slices per worker
+    kv = topkf.make_plan(topkf.FAMILY_KVSPLIT, 64, 0, splits=8)
+    cb, wb = topkf.plan_workspace_size(kv, 5, n)
+    assert wb == 5 * 2 * n * 8           # merged candidates + ping-pong per row
+    for bad in (topkf.make_plan(7, 128), topkf.make_plan(1, 32), topkf.make_plan(1, 64, dual=2),
+                topkf.make_plan(1, 64, workers=0), topkf.make_plan(2, 64, splits=0),
+                topkf.make_plan(2, 64, splits=2, min_segment=0)):
+        with pytest.raises(topkf.TopkfError):
+            topkf.plan_workspace_size(bad, 5, n)

@@ -1,0 +1,198 @@
+"""Parity of the HIP selector with the CPU oracle, through the C ABI.
+
+Exactness is the set-valued criterion of "Sample-Guided Exact Top-K Selection
+..." Eq. 30: bit-identical selected value multiset, every index strictly above
+the K-th value selected, K distinct in-range indices (or the sentinel layout
+when L <= K).  No floating-point tolerance: the selector is exact.
+"""
+import numpy as np
+import pytest
+
+from exact_row_wise_sampled_amd import workloads as W
+from tests.gpu_util import assert_exact, note, run_topk
+
+pytestmark = pytest.mark.gpu
+
+
+def topkf():
+    from exact_row_wise_sampled_amd import topkf as t
+    return t
+
+
+# ------------------------------------------------------------ full workloads
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "long", "adversarial"])
+def test_workload_auto_plan(name):
+    w = W.make(name)
+    note("workload %s M=%d N=%d K=%d auto plan" % (name, w.m, w.n, w.k))
+    out, st, _ = run_topk(w.x, w.ke, w.k, stats=True)
+    assert_exact(out, w.x, w.ke, w.k)
+    note("routes %s" % st)
+
+
+def test_workload_prefill_auto_plan():
+    w = W.make("prefill")
+    note("workload prefill M=%d N=%d auto plan" % (w.m, w.n))
+    out, st, _ = run_topk(w.x, w.ke, w.k, stats=True)
+    assert_exact(out, w.x, w.ke, w.k)
+    note("routes %s" % st)
+
+
+# -------------------------------------------------------- forced mappings
+
+def plans():
+    t = topkf()
+    P, K = t.FAMILY_PERSISTENT, t.FAMILY_KVSPLIT
+    return {
+        "pers-exact": t.make_plan(P, 0, 0, workers=7),
+        "pers-s64": t.make_plan(P, 64, 0, workers=5),
+        "pers-s64-dual": t.make_plan(P, 64, 1, workers=16),
+        "pers-s128": t.make_plan(P, 128, 0, workers=3),
+        "pers-s128-dual": t.make_plan(P, 128, 1, workers=64),
+        "kv-s128-dual-p4": t.make_plan(K, 128, 1, splits=4, min_segment=1024),
+        "kv-s64-p3": t.make_plan(K, 64, 0, splits=3, min_segment=4096),
+        "kv-s128-dual-p16": t.make_plan(K, 128, 1, splits=16, min_segment=512),
+        "kv-exact-p2": t.make_plan(K, 0, 0, splits=2, min_segment=4096),
+    }
+
+
+PLAN_NAMES = ["pers-exact", "pers-s64", "pers-s64-dual", "pers-s128", "pers-s128-dual",
+              "kv-s128-dual-p4", "kv-s64-p3", "kv-s128-dual-p16", "kv-exact-p2"]
+
+
+@pytest.mark.parametrize("plan_name", PLAN_NAMES)
+def test_mixed_rows_every_plan(plan_name):
+    """Ragged i.i.d. and adversarial rows spanning several tiles and a ragged tail."""
+    k = 256
+    n = 20000
+    lens = [0, 1, k - 1, k, k + 1, 300, 1000, 2047, 4097, 8191, 12345, 19999, 20000, 20000,
+            5000, 17001]
+    w = W.iid_normal(31, len(lens), n, lens, k)
+    adv = W.adversarial(seed=9, m=8, n=n, k=k, lo=2 * k)
+    x = np.concatenate([w.x, adv.x])
+    ke = np.concatenate([w.ke, adv.ke]).astype(np.int32)
+    note("mixed rows plan %s" % plan_name)
+    out, st, _ = run_topk(x, ke, k, plan=plans()[plan_name])
+    assert_exact(out, x, ke, k)
+    assert sum(st.values()) - st["spill"] == len(ke)
+
+
+@pytest.mark.parametrize("plan_name", PLAN_NAMES)
+def test_decode_shape_every_plan(plan_name):
+    w = W.decode(seed=12, m=24, n=65536, lo=3000)
+    note("decode-like rows plan %s" % plan_name)
+    out, st, _ = run_topk(w.x, w.ke, w.k, plan=plans()[plan_name])
+    assert_exact(out, w.x, w.ke, w.k)
+
+
+@pytest.mark.parametrize("k", [1, 2, 7, 100, 2047, 2048])
+def test_rank_values(k):
+    w = W.iid_normal(40 + k, 6, 30000, [30000, 29999, 12000, 5000, k + 1, k], k)
+    for name in ("pers-exact", "pers-s128-dual", "kv-s128-dual-p4"):
+        note("rank K=%d plan %s" % (k, name))
+        out, _, _ = run_topk(w.x, w.ke, k, plan=plans()[name])
+        assert_exact(out, w.x, w.ke, k)
+
+
+# ------------------------------------------------------------ forced routes
+
+def view_phase(row: int, s: int) -> int:
+    """The row's view residue: log2(s)-bit reversal of row mod s (Eq. 13 reading)."""
+    b = s.bit_length() - 1
+    r = row % s
+    return int(format(r, "0%db" % b)[::-1], 2)
+
+
+def aliased_rows(s: int, k: int, n: int, m: int, kind: str, seed: int = 0):
+    """Rows whose view (residue a_r) sees a misleading tail.
+
+    'band':  q view entries at 100, the next q1-q view entries at 50, and
+             enough 50s elsewhere that the secondary boundary certifies.
+    'exact': q view entries at 100 and q1-q at 50, all other values small, so
+             both boundaries underfill and exact recovery must run.
+    """
+    rng = np.random.default_rng(seed)
+    cdiv = lambda a, b: -(-a // b)
+    q = cdiv(cdiv(3 * k, 2), s)
+    q1 = cdiv(cdiv(7 * k, 4), s)
+    x = (rng.standard_normal((m, n)) * 0.1).astype(np.float32)
+    for r in range(m):
+        a = view_phase(r, s)
+        view = np.arange(a, n, s)
+        x[r, view[:q]] = 100.0 + rng.random(q).astype(np.float32)
+        x[r, view[q:q1]] = 50.0 + rng.random(q1 - q).astype(np.float32)
+        if kind == "band":
+            others = np.setdiff1d(np.arange(n), view)
+            pick = rng.choice(others, size=2 * k, replace=False)
+            x[r, pick] = 50.0 + rng.random(2 * k).astype(np.float32)
+    ke = np.full(m, n, dtype=np.int32)
+    return x, ke
+
+
+def test_route_primary_certified():
+    t = topkf()
+    w = W.iid_normal(5, 8, 65536, [65536] * 8, 2048)
+    plan = t.make_plan(t.FAMILY_PERSISTENT, 128, 1, workers=4)
+    out, st, _ = run_topk(w.x, w.ke, 2048, plan=plan)
+    assert_exact(out, w.x, w.ke, 2048)
+    assert st["primary"] >= 6, st
+
+
+@pytest.mark.parametrize("family", ["persistent", "kvsplit"])
+def test_route_band_rescue(family):
+    t = topkf()
+    k, s, n = 512, 128, 40000
+    x, ke = aliased_rows(s, k, n, 6, "band", seed=1)
+    if family == "persistent":
+        plan = t.make_plan(t.FAMILY_PERSISTENT, s, 1, workers=3)
+    else:
+        plan = t.make_plan(t.FAMILY_KVSPLIT, s, 1, splits=4, min_segment=2048)
+    note("band rescue %s" % family)
+    out, st, _ = run_topk(x, ke, k, plan=plan)
+    assert_exact(out, x, ke, k)
+    assert st["band"] == 6, st
+
+
+@pytest.mark.parametrize("family", ["persistent", "kvsplit"])
+@pytest.mark.parametrize("dual", [0, 1])
+def test_route_exact_recovery(family, dual):
+    t = topkf()
+    k, s, n = 512, 64, 40000
+    x, ke = aliased_rows(s, k, n, 5, "exact", seed=2)
+    if family == "persistent":
+        plan = t.make_plan(t.FAMILY_PERSISTENT, s, dual, workers=2)
+    else:
+        plan = t.make_plan(t.FAMILY_KVSPLIT, s, dual, splits=3, min_segment=2048)
+    note("exact recovery %s dual=%d" % (family, dual))
+    out, st, _ = run_topk(x, ke, k, plan=plan)
+    assert_exact(out, x, ke, k)
+    assert st["exact_underfill"] == 5, st
+
+
+def test_route_unusable_view_goes_exact():
+    t = topkf()
+    k = 2048
+    # |V| = ceil(L / 128) < q1 = 28 for L < 3457
+    w = W.iid_normal(8, 4, 8192, [2100, 3000, 3400, 2049], k)
+    plan = t.make_plan(t.FAMILY_PERSISTENT, 128, 1, workers=4)
+    out, st, _ = run_topk(w.x, w.ke, k, plan=plan)
+    assert_exact(out, w.x, w.ke, k)
+    assert st["exact_direct"] == 4, st
+
+
+def test_spill_rows_constant_and_quantized():
+    """Frontiers far beyond on-chip capacity: every value in one coarse bin."""
+    t = topkf()
+    k, n = 2048, 200000
+    x = np.empty((4, n), dtype=np.float32)
+    x[0] = 1.0
+    x[1] = -0.0
+    x[2] = np.float32(0.125) * np.random.default_rng(3).integers(0, 4, size=n).astype(np.float32)
+    x[3] = np.inf
+    ke = np.array([n, n - 5, n - 77, 150001], dtype=np.int32)
+    for name, plan in (("pers", t.make_plan(t.FAMILY_PERSISTENT, 128, 1, workers=2)),
+                       ("kv", t.make_plan(t.FAMILY_KVSPLIT, 128, 1, splits=8, min_segment=4096)),
+                       ("exact", t.make_plan(t.FAMILY_PERSISTENT, 0, 0, workers=4))):
+        note("spill rows plan %s" % name)
+        out, st, _ = run_topk(x, ke, k, plan=plan)
+        assert_exact(out, x, ke, k)
