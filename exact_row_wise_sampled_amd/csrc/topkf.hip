@@ -2,21 +2,22 @@
 // selector after "Sample-Guided Exact Top-K Selection for Long-Context Sparse
 // Attention" (Secs. 4-5), behind the C ABI declared in include/topkf.h.
 //
-// One 512-thread workgroup (8 wave64) works on a row at a time:
+// One 512-thread workgroup (8 wave64) works on a row (or a row segment):
 //   Phase 1 (Sec. 4.2, Eqs. 11-15; Sec. 5.2): the regular view
 //     V = {i < L : i = a_r mod s} is projected to the 11-bit coarse key and
 //     histogrammed in LDS; the first bins whose prefix reaches q = ceil(1.5K/s)
 //     and q1 = ceil(1.75K/s) give tau0 and tau1, converted once to inclusive
-//     FP32 cutoffs expressed as descending integer keys.
+//     FP32 cutoffs expressed as descending integer keys.  The first chunk of
+//     the complete-row scan is already in flight while the view is loaded.
 //   Phase 2 (Sec. 4.3, Eqs. 16-17; Sec. 5.3): one streaming pass over the
 //     row with 128-bit nontemporal loads admits key <= T0, appends the
 //     (index, key) pair to the frontier and counts its leading 11-bit digit.
-//     Underfill (C < K) appends the band T0 < key <= T1 in a second pass
-//     (Eqs. 18-19); continued underfill, an unusable view or the no-view
-//     policy take the exact coarse route (Eq. 20).
+//     Underfill (C < K) adds the band T0 < key <= T1 (Eqs. 18-19); continued
+//     underfill, an unusable view or the no-view policy take the exact coarse
+//     route (Eq. 20).
 //   Phase 3 (Sec. 4.4, Eqs. 22-25; Sec. 5.4): 11+11+10-bit refinement of the
 //     FP32 descending key over the frontier only, through two ping-pong
-//     buffers (LDS first, then a global spill slice).
+//     buffers of (index, key) pairs (LDS first, then a global spill slice).
 // Two mappings (Sec. 4.5, Sec. 5.5): a persistent pool whose workgroups take
 // rows from a device queue, and a KV-split mapping in which P workgroups scan
 // disjoint segments of one row and the last to arrive finishes it.
@@ -37,9 +38,15 @@ namespace {
 constexpr int kBlock = 512;
 constexpr int kWaves = kBlock / 64;
 constexpr int kBins = 2048;
-constexpr int kCapA = 4096;  // LDS frontier A (Q0, Q2), (index, key) pairs
-constexpr int kCapB = 2048;  // LDS frontier B (Q1)
-constexpr int kUnroll = 4;   // 128-bit loads in flight per thread
+constexpr int kFront = 7168;                 // LDS frontier, (index, key) pairs
+constexpr int kWaveCap = kFront / kWaves;    // wave-private share of it (896)
+constexpr int kWaveRegs = kWaveCap / 64;     // its entries per lane (14)
+constexpr int kRegs = 16;                    // contiguous frontier held in registers
+constexpr int kCapA = 4096;                  // general path: LDS part of Q1 / Q2
+constexpr int kRowVec = 4;      // persistent scan: 128-bit loads per thread per chunk
+constexpr int kSegVec = 8;      // KV-split scan: 128-bit loads per thread per chunk
+constexpr int kSampleVec = 8;   // view samples per thread per batch
+constexpr int kMaxSplits = 256; // KV-split parts per row
 // A NaN pattern whose descending key is 0xFFFFFFFF: larger than every cutoff,
 // so it marks lanes that hold no element.
 constexpr uint32_t kNoElem = 0xFFFFFFFFu;
@@ -47,6 +54,7 @@ constexpr uint32_t kKeyFirst = 0x007FFFFFu;  // descending key of +inf
 constexpr uint32_t kKeyLast = 0xFF800000u;   // descending key of -inf
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct Params {
     const float* logits;
@@ -66,9 +74,10 @@ struct Params {
 
 struct alignas(16) Shared {
     uint32_t hist[2][kBins];
-    uint2 qa[kCapA];
-    uint2 qb[kCapB];
+    uint2 front[kFront];
+    uint32_t offs[2][kMaxSplits + 1];  // KV-split finisher: per-part prefix offsets
     uint32_t wsum[kWaves];
+    uint32_t wcnt[kWaves];             // wave-private frontier sizes
     uint32_t res[4];
     uint32_t cnt[2];
     uint32_t out_cnt;
@@ -78,6 +87,12 @@ struct alignas(16) Shared {
     uint32_t flag;
 };
 static_assert(sizeof(Shared) <= 80 * 1024, "two workgroups per CU must fit in LDS");
+
+// Workspace geometry: every owner (a persistent worker, or a row under
+// KV-split) has two slices of slice_len(n) pairs; a wave-private frontier
+// spills into the first slice at wave_spill_len(n) pairs per wave.
+__host__ __device__ __forceinline__ int64_t wave_spill_len(int64_t n) { return (n + 7) / 8 + 8; }
+__host__ __device__ __forceinline__ int64_t slice_len(int64_t n) { return n + 128; }
 
 // ------------------------------------------------------------------ keys
 
@@ -100,21 +115,6 @@ __device__ __forceinline__ uint32_t coarse_of_bits(uint32_t b) {
     return k16 >> 5;
 }
 
-// Sec. 4.3: the inclusive FP32 cutoff of coarse bin tau, as the largest
-// non-NaN descending key whose value still has c <= tau.  c is monotone in the
-// key, so {c(x) <= tau} == {key(x) <= cutoff(tau)}.  Returns kKeyFirst - 1
-// (admits no non-NaN value) when even +inf lies above tau.
-__device__ uint32_t cutoff_key(uint32_t tau) {
-    if (coarse_of_bits(bits_of_key(kKeyFirst)) > tau) return kKeyFirst - 1;
-    if (coarse_of_bits(bits_of_key(kKeyLast)) <= tau) return kKeyLast;
-    uint32_t lo = kKeyFirst, hi = kKeyLast;  // c(lo) <= tau < c(hi)
-    while (hi - lo > 1) {
-        const uint32_t mid = lo + (hi - lo) / 2;
-        if (coarse_of_bits(bits_of_key(mid)) <= tau) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
 // Refinement digit j of a descending key: 11 + 11 + 10 bits, most
 // significant first (Sec. 4.3 "D = 3 digits of widths 11 + 11 + 10").
 __device__ __forceinline__ uint32_t digit(int j, uint32_t key) {
@@ -128,24 +128,77 @@ __device__ __forceinline__ uint32_t view_phase(uint32_t row, int s) {
     return __builtin_bitreverse32(row & (s - 1)) >> (32 - bitsn);
 }
 
+__device__ __forceinline__ uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
+// q = ceil(K~/s) with K~ = ceil(1.5K), q1 with K~1 = ceil(1.75K) (Sec. 4.2;
+// Sec. 6.4 "Conditional rescue").
+__device__ __forceinline__ uint32_t q_primary(uint32_t k, int s) {
+    return ceil_div(ceil_div(3 * k, 2), s);
+}
+__device__ __forceinline__ uint32_t q_secondary(uint32_t k, int s) {
+    return ceil_div(ceil_div(7 * k, 4), s);
+}
+
 // ------------------------------------------------------------ wave helpers
 
 __device__ __forceinline__ uint32_t lane() { return __lane_id(); }
+__device__ __forceinline__ uint32_t wave() { return threadIdx.x >> 6; }
 
 __device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// the row broadcasts of the GFX9 family.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xF, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xA, 0xF, false));
+    x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xC, 0xF, false));
+    return x;
+}
+
+// One LDS reservation for the lanes in m; returns the first reserved slot.
 __device__ __forceinline__ uint32_t wave_reserve(uint32_t* counter, uint64_t m, uint32_t n) {
     const int leader = __builtin_ctzll(m);
     uint32_t base = 0;
     if (static_cast<int>(lane()) == leader) base = atomicAdd(counter, n);
-    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), leader));
+    return readlane(base, leader);
 }
 
 __device__ __forceinline__ void lds_inc(uint32_t* h, uint32_t bin) {
     __hip_atomic_fetch_add(h + bin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void lds_add(uint32_t* h, uint32_t bin, uint32_t v) {
+    __hip_atomic_fetch_add(h + bin, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Histogram count for the lanes with pred; when they all hit one bin (constant
+// or heavily tied rows) a single add replaces 64 colliding LDS atomics.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin, bool pred, uint64_t m) {
+    const int leader = __builtin_ctzll(m);
+    const uint32_t b0 = readlane(bin, leader);
+    if (__ballot(pred && bin == b0) == m) {
+        if (static_cast<int>(lane()) == leader) lds_add(h, b0, __builtin_popcountll(m));
+    } else if (pred) {
+        lds_inc(h, bin);
+    }
+}
+
+__device__ __forceinline__ u32x2 nt_load2(const uint2* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+__device__ __forceinline__ void nt_store2(uint2* p, uint32_t a, uint32_t b) {
+    __builtin_nontemporal_store(u32x2{a, b}, reinterpret_cast<u32x2*>(p));
 }
 
 // ---------------------------------------------------------------- frontier
@@ -158,47 +211,148 @@ struct Frontier {
     uint32_t* cnt;  // LDS counter
 };
 
-__device__ __forceinline__ void fput(const Frontier& f, uint32_t slot, uint2 item) {
-    if (slot < f.cap) f.lds[slot] = item; else f.gbl[slot - f.cap] = item;
+__device__ __forceinline__ void fput(const Frontier& f, uint32_t slot, uint32_t idx, uint32_t key) {
+    if (slot < f.cap) f.lds[slot] = make_uint2(idx, key);
+    else nt_store2(f.gbl + (slot - f.cap), idx, key);
+}
+
+// Lanes with p[u] take consecutive output slots (one reservation per wave).
+__device__ __forceinline__ void commit4(const bool (&p)[4], const uint32_t (&idx)[4],
+                                        int32_t* outp, uint32_t k, Shared& sm) {
+    uint64_t m[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m[u] = __ballot(p[u]);
+    const uint64_t any = m[0] | m[1] | m[2] | m[3];
+    if (any == 0) return;
+    uint32_t c[4], tot = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { c[u] = __builtin_popcountll(m[u]); tot += c[u]; }
+    uint32_t base = wave_reserve(&sm.out_cnt, any, tot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (p[u]) {
+            const uint32_t slot = base + mbcnt(m[u]);
+            if (slot < k) outp[slot] = static_cast<int32_t>(idx[u]);
+        }
+        base += c[u];
+    }
+}
+
+// Lanes with p[u] append (idx, key) to frontier f and count bin[u] in h.
+__device__ __forceinline__ void append4(const bool (&p)[4], const uint32_t (&idx)[4],
+                                        const uint32_t (&key)[4], const uint32_t (&bin)[4],
+                                        const Frontier& f, uint32_t* h) {
+    uint64_t m[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m[u] = __ballot(p[u]);
+    const uint64_t any = m[0] | m[1] | m[2] | m[3];
+    if (any == 0) return;
+    uint32_t c[4], tot = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { c[u] = __builtin_popcountll(m[u]); tot += c[u]; }
+    uint32_t base = wave_reserve(f.cnt, any, tot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (m[u]) {
+            if (p[u]) fput(f, base + mbcnt(m[u]), idx[u], key[u]);
+            hist_add(h, bin[u], p[u], m[u]);
+        }
+        base += c[u];
+    }
+}
+
+// Visits the frontier four entries per thread at a time: g(item[4], valid[4]).
+template <class G>
+__device__ __forceinline__ void for_each4(const Frontier& f, uint32_t n, G&& g) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t nl = n < f.cap ? n : f.cap;
+    for (uint32_t e0 = 0; e0 < nl; e0 += 4 * kBlock) {
+        uint2 it[4];
+        bool v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t e = e0 + u * kBlock + tid;
+            v[u] = e < nl;
+            it[u] = v[u] ? f.lds[e] : make_uint2(0u, kNoElem);
+        }
+        g(it, v);
+    }
+    for (uint32_t e0 = nl; e0 < n; e0 += 4 * kBlock) {
+        uint2 it[4];
+        bool v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t e = e0 + u * kBlock + tid;
+            v[u] = e < n;
+            if (v[u]) {
+                const u32x2 t = nt_load2(f.gbl + (e - f.cap));
+                it[u] = make_uint2(t.x, t.y);
+            } else {
+                it[u] = make_uint2(0u, kNoElem);
+            }
+        }
+        g(it, v);
+    }
 }
 
 __device__ __forceinline__ uint2 fget(const Frontier& f, uint32_t e) {
-    return e < f.cap ? f.lds[e] : f.gbl[e - f.cap];
+    if (e < f.cap) return f.lds[e];
+    const u32x2 t = nt_load2(f.gbl + (e - f.cap));
+    return make_uint2(t.x, t.y);
 }
 
-// Output commit: lanes with `pred` take the next output slots.
-__device__ __forceinline__ void commit(bool pred, uint32_t idx, int32_t* outp, uint32_t k,
-                                       Shared& sm) {
-    const uint64_t m = __ballot(pred);
-    if (m == 0) return;
-    const uint32_t base = wave_reserve(&sm.out_cnt, m, __builtin_popcountll(m));
-    if (pred) {
-        const uint32_t slot = base + mbcnt(m);
-        if (slot < k) outp[slot] = static_cast<int32_t>(idx);
+// Wave-private frontier: wave w appends into its own share
+// front[w * kWaveCap, (w + 1) * kWaveCap) of the LDS frontier and then into its
+// own global spill range.  The running size is wave-uniform (it only changes
+// by popcounts of ballots), so placing an entry needs no atomic.
+struct WaveFrontier {
+    uint2* lds;
+    uint2* gbl;
+    uint32_t n;
+};
+
+__device__ __forceinline__ void wput(const WaveFrontier& f, uint32_t slot, uint32_t idx,
+                                     uint32_t key) {
+    if (slot < kWaveCap) f.lds[slot] = make_uint2(idx, key);
+    else nt_store2(f.gbl + (slot - kWaveCap), idx, key);
+}
+
+// Lanes with p[u] append (idx[u], key[u]) to the wave frontier and count
+// bin[u] in h.
+__device__ __forceinline__ void wappend4(const bool (&p)[4], const uint32_t (&idx)[4],
+                                         const uint32_t (&key)[4], const uint32_t (&bin)[4],
+                                         WaveFrontier& f, uint32_t* h) {
+    uint64_t m[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m[u] = __ballot(p[u]);
+    const uint64_t any = m[0] | m[1] | m[2] | m[3];
+    if (any == 0) return;
+    uint32_t base = f.n;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f.n += __builtin_popcountll(m[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (p[u]) {
+            wput(f, base + mbcnt(m[u]), idx[u], key[u]);
+            lds_inc(h, bin[u]);
+        }
+        base += __builtin_popcountll(m[u]);
     }
 }
 
-// Frontier append of (idx, key) with a histogram count of `bin` in `h`.
-__device__ __forceinline__ void append(bool pred, uint32_t idx, uint32_t key, uint32_t bin,
-                                       const Frontier& f, uint32_t* h) {
-    const uint64_t m = __ballot(pred);
-    if (m == 0) return;
-    const uint32_t base = wave_reserve(f.cnt, m, __builtin_popcountll(m));
-    if (pred) {
-        fput(f, base + mbcnt(m), make_uint2(idx, key));
-        lds_inc(h, bin);
-    }
-}
+// ------------------------------------------------------------ block scans
 
-// ------------------------------------------------------------ block scan
+__device__ __forceinline__ void clear_hist(uint32_t* h) {
+    reinterpret_cast<uint4*>(h)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+}
 
 // For each target t[i] (1 <= t[i] <= sum of hist), finds b = min{b : H(b) >=
 // t[i]} and H(b - 1) (Eqs. 15, 23), written to sm.res[2i], sm.res[2i + 1].
 // Each thread owns 4 consecutive bins.  Reads hist before its first barrier
 // and ends with a barrier, so hist may be rewritten right after it returns.
 template <int NT>
-__device__ void block_find(const uint32_t* hist, const uint32_t (&t)[NT], Shared& sm) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t (&t)[NT], Shared& sm) {
+    const uint32_t tid = threadIdx.x;
     // Defaults keep every later LDS index in range should a target exceed
     // the histogram total (only possible for NaN inputs, which the contract
     // excludes); the finding thread overwrites them after the first barrier.
@@ -208,16 +362,11 @@ __device__ void block_find(const uint32_t* hist, const uint32_t (&t)[NT], Shared
     }
     const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];
     const uint32_t s = v.x + v.y + v.z + v.w;
-    uint32_t incl = s;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d);
-        if (static_cast<int>(lane()) >= d) incl += o;
-    }
-    if (lane() == 63) sm.wsum[tid >> 6] = incl;
+    const uint32_t incl = wave_incl_scan(s);
+    if (lane() == 63) sm.wsum[wave()] = incl;
     __syncthreads();
     uint32_t base = 0;
-    for (int w = 0; w < (tid >> 6); ++w) base += sm.wsum[w];
+    for (uint32_t w = 0; w < wave(); ++w) base += sm.wsum[w];
     const uint32_t excl = base + incl - s;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -237,75 +386,134 @@ __device__ void block_find(const uint32_t* hist, const uint32_t (&t)[NT], Shared
     __syncthreads();
 }
 
-__device__ __forceinline__ void clear_hist(uint32_t* h) {
-    reinterpret_cast<uint4*>(h)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+// Exclusive prefix of one value per thread over the block; *total gets the sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, Shared& sm) {
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane() == 63) sm.wsum[wave()] = incl;
+    __syncthreads();
+    uint32_t base = 0, all = 0;
+    for (uint32_t w = 0; w < kWaves; ++w) {
+        const uint32_t ws = sm.wsum[w];
+        if (w < wave()) base += ws;
+        all += ws;
+    }
+    __syncthreads();
+    *total = all;
+    return base + incl - v;
+}
+
+// Sec. 4.3: the inclusive FP32 cutoff of coarse bin tau, as the largest
+// non-NaN descending key whose value still has c <= tau.  c is monotone in the
+// key, so {c(x) <= tau} == {key(x) <= cutoff(tau)}.  A 64-way search by one
+// whole wave: each round splits the interval over the lanes.  Returns
+// kKeyFirst - 1 (admits no non-NaN value) when even +inf lies above tau.
+__device__ __forceinline__ uint32_t wave_cutoff(uint32_t tau) {
+    if (coarse_of_bits(bits_of_key(kKeyFirst)) > tau) return kKeyFirst - 1;
+    if (coarse_of_bits(bits_of_key(kKeyLast)) <= tau) return kKeyLast;
+    uint32_t lo = kKeyFirst, hi = kKeyLast;  // c(lo) <= tau < c(hi)
+    while (hi - lo > 1) {
+        const uint32_t step = (hi - lo + 63) / 64;
+        const uint32_t probe = lo + (lane() + 1) * step;
+        const bool ok = probe < hi && coarse_of_bits(bits_of_key(probe)) <= tau;
+        const uint32_t nt = __builtin_popcountll(__ballot(ok));
+        if (nt < 64) {
+            const uint32_t nhi = lo + (nt + 1) * step;  // the first failing probe
+            if (nhi < hi) hi = nhi;
+        }
+        lo += nt * step;
+    }
+    return lo;
 }
 
 // ------------------------------------------------------------- streaming
 
-// Calls f(bits4, index_of_bits4.x) over elements [lo, hi) of row x: 128-bit
-// nontemporal loads for the 16-byte aligned body, one element per lane for
-// the unaligned head and the tail.  Lanes without an element see kNoElem.
-// Every thread of the block must call it with the same arguments.
-template <class F>
-__device__ __forceinline__ void stream_range(const float* x, uint32_t lo, uint32_t hi, F&& f) {
-    if (hi <= lo) return;
+// [lo, hi) of row x split for 128-bit loads: an unaligned head of up to 3
+// elements, a 16-byte aligned body of nvec vectors, a tail of up to 3.
+struct Span {
+    const float* x;
+    uint32_t lo, hi, head, vlo, nvec, tlo, nscal;
+};
+
+__device__ __forceinline__ Span make_span(const float* x, uint32_t lo, uint32_t hi) {
+    Span s;
+    s.x = x;
+    s.lo = lo;
+    s.hi = hi > lo ? hi : lo;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(x + lo);
     uint32_t head = static_cast<uint32_t>(((16u - (addr & 15u)) & 15u) >> 2);
-    if (head > hi - lo) head = hi - lo;
-    const uint32_t vlo = lo + head;
-    const uint32_t nvec = (hi - vlo) >> 2;
-    const uint32_t tlo = vlo + 4 * nvec;
-    const u32x4* xv = reinterpret_cast<const u32x4*>(x + vlo);
-    const uint32_t tid = threadIdx.x;
-    for (uint32_t base = 0; base < nvec; base += kBlock * kUnroll) {
-        u32x4 v[kUnroll];
+    if (head > s.hi - lo) head = s.hi - lo;
+    s.head = head;
+    s.vlo = lo + head;
+    s.nvec = (s.hi - s.vlo) >> 2;
+    s.tlo = s.vlo + 4 * s.nvec;
+    s.nscal = head + (s.hi - s.tlo);
+    return s;
+}
+
+template <int U>
+__device__ __forceinline__ void load_chunk(const Span& sp, uint32_t base, u32x4 (&v)[U]) {
+    const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t vi = base + u * kBlock + tid;
-            if (vi < nvec) v[u] = __builtin_nontemporal_load(xv + vi);
-            else v[u] = u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) f(v[u], vlo + 4 * (base + u * kBlock + tid));
-    }
-    const uint32_t nscal = head + (hi - tlo);
-    if (nscal) {
-        const uint32_t e = tid < head ? lo + tid : tlo + (tid - head);
-        const uint32_t b = tid < nscal ? __float_as_uint(x[e]) : kNoElem;
-        f(u32x4{b, kNoElem, kNoElem, kNoElem}, e);
+    for (int u = 0; u < U; ++u) {
+        const uint32_t vi = base + u * kBlock + threadIdx.x;
+        if (vi < sp.nvec) v[u] = __builtin_nontemporal_load(xv + vi);
+        else v[u] = u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
     }
 }
 
+// Calls f(bits4, index of bits4.x) over every element of the span, with the
+// first chunk (U vectors per thread) and the head/tail elements loaded before
+// pre() runs, so their latency overlaps pre().  Later chunks are double
+// buffered: the next chunk is in flight while the current one is processed.
+// Every thread of the block must call it with the same span.
+template <int U, class Pre, class F>
+__device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f) {
+    const uint32_t tid = threadIdx.x;
+    u32x4 cur[U];
+    if (sp.nvec) load_chunk<U>(sp, 0, cur);
+    const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
+    uint32_t sb = kNoElem;
+    if (tid < sp.nscal) sb = __float_as_uint(sp.x[se]);
+    pre();
+    if (sp.nscal) f(u32x4{sb, kNoElem, kNoElem, kNoElem}, se);
+    for (uint32_t base = 0; base < sp.nvec; base += kBlock * U) {
+        const bool more = base + kBlock * U < sp.nvec;
+        u32x4 nxt[U];
+        if (more) load_chunk<U>(sp, base + kBlock * U, nxt);
+#pragma unroll
+        for (int u = 0; u < U; ++u) f(cur[u], sp.vlo + 4 * (base + u * kBlock + tid));
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+    }
+}
+
+struct NoPre {
+    __device__ void operator()() const {}
+};
+
 // Phase 2 admission of one 4-element group: key <= hi (and key > lo for the
-// band pass of Eq. 18), appended to frontier f with its leading digit counted
-// in h (Eq. 17).  One LDS reservation per wave and group.
+// band of Eq. 18), appended to the wave frontier with its leading digit
+// counted in h (Eq. 17).
 template <bool BAND>
 __device__ __forceinline__ void admit4(u32x4 b, uint32_t i0, uint32_t klo, uint32_t khi,
-                                       const Frontier& f, uint32_t* h) {
-    const uint32_t k0 = desc_key(b.x), k1 = desc_key(b.y), k2 = desc_key(b.z), k3 = desc_key(b.w);
-    const bool p0 = k0 <= khi && (!BAND || k0 > klo);
-    const bool p1 = k1 <= khi && (!BAND || k1 > klo);
-    const bool p2 = k2 <= khi && (!BAND || k2 > klo);
-    const bool p3 = k3 <= khi && (!BAND || k3 > klo);
-    const uint64_t m0 = __ballot(p0), m1 = __ballot(p1), m2 = __ballot(p2), m3 = __ballot(p3);
-    const uint64_t any = m0 | m1 | m2 | m3;
-    if (any == 0) return;
-    const uint32_t c0 = __builtin_popcountll(m0), c1 = __builtin_popcountll(m1);
-    const uint32_t c2 = __builtin_popcountll(m2), c3 = __builtin_popcountll(m3);
-    uint32_t base = wave_reserve(f.cnt, any, c0 + c1 + c2 + c3);
-    if (p0) { fput(f, base + mbcnt(m0), make_uint2(i0, k0)); lds_inc(h, k0 >> 21); }
-    base += c0;
-    if (p1) { fput(f, base + mbcnt(m1), make_uint2(i0 + 1, k1)); lds_inc(h, k1 >> 21); }
-    base += c1;
-    if (p2) { fput(f, base + mbcnt(m2), make_uint2(i0 + 2, k2)); lds_inc(h, k2 >> 21); }
-    base += c2;
-    if (p3) { fput(f, base + mbcnt(m3), make_uint2(i0 + 3, k3)); lds_inc(h, k3 >> 21); }
+                                       WaveFrontier& f, uint32_t* h) {
+    uint32_t key[4], idx[4], bin[4];
+    bool p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        key[u] = desc_key(b[u]);
+        p[u] = key[u] <= khi && (!BAND || key[u] > klo);
+        idx[u] = i0 + u;
+        bin[u] = key[u] >> 21;
+    }
+    wappend4(p, idx, key, bin, f, h);
 }
 
 // ------------------------------------------------------------ row pieces
 
-__device__ void sentinel_row(int32_t* outp, uint32_t L, uint32_t k) {
+__device__ __forceinline__ void sentinel_row(int32_t* outp, uint32_t L, uint32_t k) {
     for (uint32_t j = threadIdx.x; j < k; j += kBlock) outp[j] = j < L ? static_cast<int32_t>(j) : -1;
 }
 
@@ -313,63 +521,165 @@ __device__ __forceinline__ void count_route(const Params& p, int route) {
     if (p.stats && threadIdx.x == 0) atomicAdd(p.stats + route, 1u);
 }
 
-// Phase 1: coarse histogram of the view into h (already cleared and visible),
-// then tau0/tau1 and their cutoffs into sm.cut.  Ends with a barrier.
-__device__ void phase1(const float* x, uint32_t a, uint32_t nv, int s, uint32_t q, uint32_t q1,
+// Phase 1: coarse histogram of the view into h (cleared and visible), then
+// tau0/tau1 and their cutoffs into sm.cut[0], sm.cut[1].  All sample loads of
+// a batch are issued before any is used.  Ends with a barrier.
+__device__ __forceinline__ void phase1(const float* x, uint32_t a, uint32_t nv, int s, uint32_t q, uint32_t q1,
                        uint32_t* h, Shared& sm) {
-    for (uint32_t j = threadIdx.x; j < nv; j += kBlock)
-        lds_inc(h, coarse_of_bits(__float_as_uint(x[a + j * s])));
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t j0 = 0; j0 < nv; j0 += kBlock * kSampleVec) {
+        uint32_t b[kSampleVec];
+#pragma unroll
+        for (int u = 0; u < kSampleVec; ++u) {
+            const uint32_t j = j0 + u * kBlock + tid;
+            b[u] = j < nv ? __float_as_uint(x[a + j * s]) : kNoElem;
+        }
+#pragma unroll
+        for (int u = 0; u < kSampleVec; ++u)
+            if (b[u] != kNoElem) lds_inc(h, coarse_of_bits(b[u]));
+    }
     __syncthreads();
     const uint32_t t[2] = {q, q1};
     block_find<2>(h, t, sm);
-    if (threadIdx.x == 0) {
-        const uint32_t tau0 = sm.res[0], tau1 = sm.res[2];
-        sm.cut[0] = cutoff_key(tau0);
-        sm.cut[1] = tau1 > tau0 ? cutoff_key(tau1) : sm.cut[0];
+    const uint32_t tau0 = sm.res[0], tau1 = sm.res[2];
+    if (wave() < 2) {
+        const uint32_t c = wave_cutoff(wave() == 0 ? tau0 : tau1);
+        if (lane() == 0) sm.cut[wave()] = c;
     }
     __syncthreads();
 }
 
+// Records each wave's frontier size and returns the total (ends with a barrier).
+__device__ __forceinline__ uint32_t publish_waves(const WaveFrontier& wf, Shared& sm) {
+    if (lane() == 0) sm.wcnt[wave()] = wf.n;
+    __syncthreads();
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) c += sm.wcnt[w];
+    return c;
+}
+
 // Exact coarse route (Sec. 4.3, Eq. 20) over [0, L): coarse histogram of
 // every value, tau* = min{b : C(b) >= K}, then one classification pass that
-// commits c < tau* to the output and retains c == tau* in frontier A with its
-// leading-digit histogram in h0.  Returns k0 = K - |E0|.
-__device__ uint32_t exact_route(const float* x, uint32_t L, uint32_t k, int32_t* outp,
-                                const Frontier& A, uint32_t* hc, uint32_t* h0, Shared& sm) {
-    __syncthreads();  // earlier readers of the frontier count and histograms are done
+// commits c < tau* to the output and retains c == tau* in the wave frontier
+// with its leading-digit histogram in h0.  Returns k0 = K - |E0|; the
+// committed count is left in sm.out_cnt and the frontier sizes in sm.wcnt.
+__device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint32_t k,
+                                                int32_t* outp, WaveFrontier& wf, uint32_t* hc,
+                                                uint32_t* h0, Shared& sm) {
+    __syncthreads();  // earlier readers of the frontier and histograms are done
     clear_hist(hc);
     clear_hist(h0);
-    if (threadIdx.x == 0) { *A.cnt = 0; sm.out_cnt = 0; }
+    if (threadIdx.x == 0) sm.out_cnt = 0;
+    wf.n = 0;
     __syncthreads();
-    stream_range(x, 0, L, [&](u32x4 b, uint32_t) {
-        if (b.x != kNoElem) lds_inc(hc, coarse_of_bits(b.x));
-        if (b.y != kNoElem) lds_inc(hc, coarse_of_bits(b.y));
-        if (b.z != kNoElem) lds_inc(hc, coarse_of_bits(b.z));
-        if (b.w != kNoElem) lds_inc(hc, coarse_of_bits(b.w));
+    const Span sp = make_span(x, 0, L);
+    scan_span<kRowVec>(sp, NoPre{}, [&](u32x4 b, uint32_t) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (b[u] != kNoElem) lds_inc(hc, coarse_of_bits(b[u]));
     });
     __syncthreads();
     const uint32_t t[1] = {k};
     block_find<1>(hc, t, sm);
     const uint32_t tau = sm.res[0], before = sm.res[1];
-    stream_range(x, 0, L, [&](u32x4 b, uint32_t i0) {
+    scan_span<kRowVec>(sp, NoPre{}, [&](u32x4 b, uint32_t i0) {
+        bool com[4], ret[4];
+        uint32_t idx[4], key[4], bin[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t bc = b[c];
-            const bool valid = bc != kNoElem;
-            const uint32_t cc = coarse_of_bits(bc);
-            commit(valid && cc < tau, i0 + c, outp, k, sm);
-            const uint32_t key = desc_key(bc);
-            append(valid && cc == tau, i0 + c, key, key >> 21, A, h0);
+        for (int u = 0; u < 4; ++u) {
+            const bool valid = b[u] != kNoElem;
+            const uint32_t cc = coarse_of_bits(b[u]);
+            com[u] = valid && cc < tau;
+            ret[u] = valid && cc == tau;
+            idx[u] = i0 + u;
+            key[u] = desc_key(b[u]);
+            bin[u] = key[u] >> 21;
         }
+        commit4(com, idx, outp, k, sm);
+        wappend4(ret, idx, key, bin, wf, h0);
     });
-    __syncthreads();
+    publish_waves(wf, sm);
     return k - before;
 }
 
-// Phase 3 (Sec. 4.4): refinement of frontier `cur` whose leading-digit
+// Phase 3 (Sec. 4.4) with the whole frontier in registers: each thread holds
+// up to R (index, key) entries given by load(u, idx, key).  hc holds the
+// leading-digit histogram of all entries, kq is the remaining quota and
+// out_base the number of indices committed so far.  Each round finds b_j
+// (Eq. 23), commits the lower digit groups (Eq. 24) and keeps the boundary
+// group (Eq. 25) while counting its next digit; output slots come from block
+// prefix sums.  After the last digit the boundary group holds equal keys and
+// its first `need` entries fill the output.  Commits exactly kq indices.
+template <int R, class Load>
+__device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t* hn, uint32_t kq,
+                                            uint32_t out_base, int32_t* outp, uint32_t k,
+                                            Shared& sm) {
+    uint32_t idx[R], key[R];
+    uint32_t act = 0;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        idx[u] = 0;
+        key[u] = kNoElem;
+        if (load(u, idx[u], key[u])) act |= 1u << u;
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        if (j < 2) clear_hist(hn);
+        const uint32_t t[1] = {kq};
+        block_find<1>(hc, t, sm);
+        const uint32_t b = sm.res[0], before = sm.res[1];
+        const uint32_t inb = hc[b];
+        const bool exact_fill = before + inb == kq;  // the boundary group fits exactly
+        const bool last = exact_fill || j == 2;
+        const uint32_t need = kq - before;
+        uint32_t com = 0, tie = 0, keep = 0;
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const uint32_t d = digit(j, key[u]);
+            const bool on = (act >> u) & 1u;
+            if (on && (d < b || (exact_fill && d == b))) com |= 1u << u;
+            if (on && !exact_fill && d == b) {
+                if (last) tie |= 1u << u;
+                else keep |= 1u << u;
+            }
+        }
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(
+            static_cast<uint32_t>(__builtin_popcount(com)) |
+                (static_cast<uint32_t>(__builtin_popcount(tie)) << 16),
+            &tot, sm);
+        const uint32_t tot_c = tot & 0xFFFFu;
+        uint32_t pc = out_base + (ex & 0xFFFFu);
+        uint32_t pt = ex >> 16;
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            if ((com >> u) & 1u) {
+                if (pc < k) outp[pc] = static_cast<int32_t>(idx[u]);
+                ++pc;
+            }
+            if ((tie >> u) & 1u) {
+                const uint32_t slot = out_base + tot_c + pt;
+                if (pt < need && slot < k) outp[slot] = static_cast<int32_t>(idx[u]);
+                ++pt;
+            }
+        }
+        if (last) break;
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+            if ((keep >> u) & 1u) lds_inc(hn, digit(j + 1, key[u]));
+        act = keep;
+        out_base += tot_c;
+        kq = need;
+        __syncthreads();
+        uint32_t* th = hc; hc = hn; hn = th;
+    }
+}
+
+// Phase 3 (Sec. 4.4), general form: refinement of frontier `cur` whose leading-digit
 // histogram is in hc, with remaining quota kq.  Frontier counts and hc must
 // be visible (barrier done).  Commits exactly kq more indices.
-__device__ void refine(Frontier cur, Frontier nxt, uint32_t* hc, uint32_t* hn, uint32_t kq,
+__device__ __forceinline__ void refine(Frontier cur, Frontier nxt, uint32_t* hc, uint32_t* hn, uint32_t kq,
                        int32_t* outp, uint32_t k, Shared& sm) {
     const uint32_t tid = threadIdx.x;
     for (int j = 0; j < 3; ++j) {
@@ -383,33 +693,137 @@ __device__ void refine(Frontier cur, Frontier nxt, uint32_t* hc, uint32_t* hn, u
         const bool exact_fill = before + inb == kq;  // the boundary group fits exactly
         const bool last = exact_fill || j == 2;
         const uint32_t need = kq - before;
-        for (uint32_t e0 = 0; e0 < n; e0 += kBlock) {
-            const uint32_t e = e0 + tid;
-            const bool valid = e < n;
-            const uint2 it = valid ? fget(cur, e) : make_uint2(0u, 0u);
-            const uint32_t d = digit(j, it.y);
-            if (last) {
-                bool take = valid && (exact_fill ? d <= b : d < b);
-                if (!exact_fill) {
-                    const bool tie = valid && d == b;
-                    const uint64_t m = __ballot(tie);
-                    if (m) {
-                        const uint32_t base = wave_reserve(&sm.tie_cnt, m, __builtin_popcountll(m));
-                        if (tie && base + mbcnt(m) < need) take = true;
+        if (inb == n && !exact_fill) {
+            // The whole frontier shares digit j (so before == 0): nothing is
+            // committed or discarded in this round.
+            if (j == 2) {
+                // All keys are equal: any `need` entries complete the output.
+                const uint32_t base = sm.out_cnt;
+                for (uint32_t e = tid; e < need; e += kBlock)
+                    if (base + e < k) outp[base + e] = static_cast<int32_t>(fget(cur, e).x);
+                __syncthreads();
+                break;
+            }
+            // Q_{j+1} = Q_j: keep the frontier in place and count digit j+1.
+            for_each4(cur, n, [&](const uint2 (&it)[4], const bool (&v)[4]) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint64_t m = __ballot(v[u]);
+                    if (m) hist_add(hn, digit(j + 1, it[u].y), v[u], m);
+                }
+            });
+            __syncthreads();
+            uint32_t* th = hc; hc = hn; hn = th;
+            continue;
+        }
+        for_each4(cur, n, [&](const uint2 (&it)[4], const bool (&v)[4]) {
+            bool take[4], keep[4];
+            uint32_t idx[4], key[4], bin[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t d = digit(j, it[u].y);
+                idx[u] = it[u].x;
+                key[u] = it[u].y;
+                take[u] = v[u] && (last && exact_fill ? d <= b : d < b);
+                keep[u] = v[u] && d == b && !last;
+                bin[u] = last ? 0u : digit(j + 1, it[u].y);
+            }
+            if (last && !exact_fill) {
+                // Final digit: the boundary group holds equal keys; take the
+                // first `need` of them in reservation order.
+                bool tie[4];
+                uint64_t m[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    tie[u] = v[u] && digit(j, it[u].y) == b;
+                    m[u] = __ballot(tie[u]);
+                }
+                const uint64_t any = m[0] | m[1] | m[2] | m[3];
+                if (any) {
+                    uint32_t tot = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) tot += __builtin_popcountll(m[u]);
+                    uint32_t base = wave_reserve(&sm.tie_cnt, any, tot);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (tie[u] && base + mbcnt(m[u]) < need) take[u] = true;
+                        base += __builtin_popcountll(m[u]);
                     }
                 }
-                commit(take, it.x, outp, k, sm);
-            } else {
-                commit(valid && d < b, it.x, outp, k, sm);
-                append(valid && d == b, it.x, it.y, digit(j + 1, it.y), nxt, hn);
             }
-        }
+            commit4(take, idx, outp, k, sm);
+            if (!last) append4(keep, idx, key, bin, nxt, hn);
+        });
         __syncthreads();
         if (last) break;
         kq = need;
         const Frontier tf = cur; cur = nxt; nxt = tf;
         uint32_t* th = hc; hc = hn; hn = th;
     }
+}
+
+// Copies every wave's frontier entries (LDS share, then its spill) into
+// dst[0, C) in wave order.  Ends with a barrier.
+__device__ __forceinline__ void compact_waves(const uint2* spill_base, int64_t spill_len,
+                                              uint2* dst, Shared& sm) {
+    if (threadIdx.x == 0) {
+        uint32_t o = 0;
+        for (int w = 0; w < kWaves; ++w) { sm.offs[0][w] = o; o += sm.wcnt[w]; }
+        sm.offs[0][kWaves] = o;
+    }
+    __syncthreads();
+    const uint32_t C = sm.offs[0][kWaves];
+    for (uint32_t g = threadIdx.x; g < C; g += kBlock) {
+        uint32_t w = 0;
+        while (w + 1 < kWaves && sm.offs[0][w + 1] <= g) ++w;
+        const uint32_t e = g - sm.offs[0][w];
+        uint2 v;
+        if (e < kWaveCap) {
+            v = sm.front[w * kWaveCap + e];
+        } else {
+            const u32x2 t = nt_load2(spill_base + w * spill_len + (e - kWaveCap));
+            v = make_uint2(t.x, t.y);
+        }
+        nt_store2(dst + g, v.x, v.y);
+    }
+    __syncthreads();
+}
+
+// Phase 3 for a wave-private frontier of C entries (sizes in sm.wcnt, visible),
+// leading-digit histogram h1, quota kq, sm.out_cnt indices already committed.
+// When every wave's share fits on chip the frontier is refined from
+// registers; otherwise it is gathered into `contig` and refined through
+// ping-pong buffers (LDS, then `spare`).  spill_base/spill_len locate the
+// wave spills; `spare` may overlap them.
+__device__ __forceinline__ void finish_waves(uint32_t C, const uint2* spill_base,
+                                             int64_t spill_len, uint2* contig, uint2* spare,
+                                             uint32_t* h1, uint32_t* h0, uint32_t kq,
+                                             int32_t* outp, uint32_t k, Shared& sm) {
+    const uint32_t out_base = sm.out_cnt;
+    uint32_t wmax = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wmax = sm.wcnt[w] > wmax ? sm.wcnt[w] : wmax;
+    if (wmax <= static_cast<uint32_t>(kWaveCap)) {
+        const uint32_t mine = sm.wcnt[wave()];
+        const uint2* reg = sm.front + wave() * kWaveCap;
+        refine_regs<kWaveRegs>(
+            [&](int u, uint32_t& i, uint32_t& key) {
+                const uint32_t e = lane() + 64 * u;
+                if (e >= mine) return false;
+                const uint2 v = reg[e];
+                i = v.x;
+                key = v.y;
+                return true;
+            },
+            h1, h0, kq, out_base, outp, k, sm);
+        return;
+    }
+    compact_waves(spill_base, spill_len, contig, sm);
+    if (threadIdx.x == 0) sm.cnt[0] = C;
+    __syncthreads();
+    const Frontier cur{sm.front, 0, contig, &sm.cnt[0]};
+    const Frontier nxt{sm.front, kCapA, spare, &sm.cnt[1]};
+    refine(cur, nxt, h1, h0, kq, outp, k, sm);
 }
 
 // Number of view samples and the view's phase for a row.
@@ -419,52 +833,60 @@ __device__ __forceinline__ uint32_t view_size(uint32_t row, uint32_t L, uint32_t
     return L > *a ? (L - *a + S - 1) / S : 0u;
 }
 
-__device__ __forceinline__ uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+__device__ __forceinline__ uint32_t clamp_len(int32_t v, int32_t n) {
+    return static_cast<uint32_t>(v < 0 ? 0 : (v > n ? n : v));
+}
 
-// q = ceil(K~/s) with K~ = ceil(1.5K), q1 with K~1 = ceil(1.75K) (Sec. 4.2;
-// Sec. 6.4 "Conditional rescue").
-__device__ __forceinline__ uint32_t q_primary(uint32_t k, int s) { return ceil_div(ceil_div(3 * k, 2), s); }
-__device__ __forceinline__ uint32_t q_secondary(uint32_t k, int s) { return ceil_div(ceil_div(7 * k, 4), s); }
-
-// One row, whole-row ownership (persistent mapping).
+// One row, whole-row ownership (persistent mapping).  sliceA holds the wave
+// spills, sliceB is the contiguous frontier of the general path.
 template <int S, bool DUAL>
-__device__ void select_row(const Params& p, int row, Shared& sm, const Frontier& A,
-                           const Frontier& B) {
+__device__ __forceinline__ void select_row(const Params& p, int row, Shared& sm, uint2* sliceA,
+                                           uint2* sliceB) {
     const uint32_t k = p.k;
     int32_t* outp = p.out + static_cast<int64_t>(row) * k;
-    int32_t Ls = p.ke[row];
-    const uint32_t L = static_cast<uint32_t>(Ls < 0 ? 0 : (Ls > p.n ? p.n : Ls));
+    const uint32_t L = clamp_len(p.ke[row], p.n);
     if (L <= k) {
         sentinel_row(outp, L, k);
         count_route(p, TOPKF_ROUTE_SENTINEL);
         return;
     }
     const float* x = p.logits + static_cast<int64_t>(row) * p.stride;
+    const int64_t wsl = wave_spill_len(p.n);
     uint32_t* h0 = sm.hist[0];
     uint32_t* h1 = sm.hist[1];
+    WaveFrontier wf{sm.front + wave() * kWaveCap, sliceA + wave() * wsl, 0};
     int route = TOPKF_ROUTE_EXACT_DIRECT;
     bool certified = false;
+    uint32_t C = 0;
     if constexpr (S > 0) {
         uint32_t a;
         const uint32_t nv = view_size<S>(row, L, &a);
         const uint32_t q = q_primary(k, S), q1 = DUAL ? q_secondary(k, S) : q;
         if (nv >= q1) {
-            clear_hist(h0);
-            clear_hist(h1);
-            if (threadIdx.x == 0) { *A.cnt = 0; sm.out_cnt = 0; }
-            __syncthreads();
-            phase1(x, a, nv, S, q, q1, h0, sm);
-            const uint32_t T0 = sm.cut[0], T1 = sm.cut[1];
-            stream_range(x, 0, L, [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, A, h1); });
-            __syncthreads();
-            uint32_t C = *A.cnt;
+            uint32_t T0 = 0, T1 = 0;
+            const Span sp = make_span(x, 0, L);
+            scan_span<kRowVec>(
+                sp,
+                [&]() {
+                    clear_hist(h0);
+                    clear_hist(h1);
+                    if (threadIdx.x == 0) sm.out_cnt = 0;
+                    __syncthreads();
+                    phase1(x, a, nv, S, q, q1, h0, sm);
+                    T0 = sm.cut[0];
+                    T1 = sm.cut[1];
+                },
+                [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, wf, h1); });
+            C = publish_waves(wf, sm);
             route = TOPKF_ROUTE_PRIMARY;
             if (C < k) {
                 route = TOPKF_ROUTE_EXACT_UNDERFILL;
                 if (DUAL && T1 > T0) {
-                    stream_range(x, 0, L, [&](u32x4 b, uint32_t i0) { admit4<true>(b, i0, T0, T1, A, h1); });
+                    scan_span<kRowVec>(sp, NoPre{}, [&](u32x4 b, uint32_t i0) {
+                        admit4<true>(b, i0, T0, T1, wf, h1);
+                    });
                     __syncthreads();
-                    C = *A.cnt;
+                    C = publish_waves(wf, sm);
                     if (C >= k) route = TOPKF_ROUTE_BAND;
                 }
             }
@@ -472,24 +894,30 @@ __device__ void select_row(const Params& p, int row, Shared& sm, const Frontier&
         }
     }
     uint32_t kq = k;
-    if (!certified) kq = exact_route(x, L, k, outp, A, h0, h1, sm);
+    if (!certified) {
+        kq = exact_route(x, L, k, outp, wf, h0, h1, sm);
+        C = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) C += sm.wcnt[w];
+    }
     count_route(p, route);
-    if (*A.cnt > A.cap) count_route(p, TOPKF_ROUTE_SPILL);
-    refine(A, B, h1, h0, kq, outp, k, sm);
+    bool spill = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
+    if (spill) count_route(p, TOPKF_ROUTE_SPILL);
+    finish_waves(C, sliceA, wsl, sliceB, sliceA, h1, h0, kq, outp, k, sm);
 }
 
 template <int S, bool DUAL>
 __global__ __launch_bounds__(kBlock) void persistent_kernel(Params p) {
     __shared__ Shared sm;
     const uint32_t G = gridDim.x;
-    int32_t ml = *p.num_valid_rows;
-    const int m_live = ml < 0 ? 0 : (ml > p.m_cap ? p.m_cap : ml);
-    const int64_t slice = static_cast<int64_t>(p.n);
-    const Frontier A{sm.qa, kCapA, p.ws + (2 * static_cast<int64_t>(blockIdx.x)) * slice, &sm.cnt[0]};
-    const Frontier B{sm.qb, kCapB, p.ws + (2 * static_cast<int64_t>(blockIdx.x) + 1) * slice, &sm.cnt[1]};
+    const int m_live = static_cast<int>(clamp_len(*p.num_valid_rows, p.m_cap));
+    uint2* sliceA = p.ws + 2 * static_cast<int64_t>(blockIdx.x) * slice_len(p.n);
+    uint2* sliceB = sliceA + slice_len(p.n);
     int row = blockIdx.x;  // first wave: one row each; then the queue
     while (row < m_live) {
-        select_row<S, DUAL>(p, row, sm, A, B);
+        select_row<S, DUAL>(p, row, sm, sliceA, sliceB);
         __syncthreads();
         if (threadIdx.x == 0) sm.next_row = static_cast<int32_t>(G + atomicAdd(p.counters, 1u));
         __syncthreads();
@@ -507,10 +935,21 @@ __global__ __launch_bounds__(kBlock) void persistent_kernel(Params p) {
     }
 }
 
+// Bounds of part `part` of Pr near-equal contiguous segments of [0, L),
+// aligned to 4 elements (Sec. 4.5: disjoint contiguous segments).
+__device__ __forceinline__ uint32_t segment_chunk(uint32_t L, uint32_t Pr) {
+    return ceil_div(ceil_div(L, Pr), 4) * 4;
+}
+
 // KV-split mapping (Sec. 4.5, Eqs. 26-27; Sec. 5.5 "Sampled KV-split").
 // Workgroups are numbered so that the parts of a row sit on one XCD (the
 // dispatcher deals workgroup ids round-robin over the 8 XCDs), so the
 // replicated view and the finisher's reads stay in that XCD's L2.
+// Each part scans its segment once with the view's tau0/tau1 and writes the
+// admitted (index, key) pairs into its own range of the row's region:
+// primary candidates upward from the segment start, band candidates
+// (T0 < key <= T1) downward from the segment end.  The last part to arrive
+// gathers them into LDS, counts their leading digit and refines.
 template <int S, bool DUAL>
 __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
     __shared__ Shared sm;
@@ -519,13 +958,11 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
     const uint32_t li = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const uint32_t row = li / P, part = li % P;
     if (row >= static_cast<uint32_t>(p.m_cap)) return;
-    int32_t ml = *p.num_valid_rows;
-    const uint32_t m_live = static_cast<uint32_t>(ml < 0 ? 0 : (ml > p.m_cap ? p.m_cap : ml));
+    const uint32_t m_live = clamp_len(*p.num_valid_rows, p.m_cap);
     if (row >= m_live) return;
     const uint32_t k = p.k;
     int32_t* outp = p.out + static_cast<int64_t>(row) * k;
-    const int32_t Ls = p.ke[row];
-    const uint32_t L = static_cast<uint32_t>(Ls < 0 ? 0 : (Ls > p.n ? p.n : Ls));
+    const uint32_t L = clamp_len(p.ke[row], p.n);
     if (L <= k) {
         if (part == 0) {
             sentinel_row(outp, L, k);
@@ -534,14 +971,14 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
         return;
     }
     const float* x = p.logits + static_cast<int64_t>(row) * p.stride;
-    uint2* region = p.ws + 2 * static_cast<int64_t>(row) * p.n;  // merged candidates
-    uint2* region2 = region + p.n;                                // spill / ping-pong
-    uint32_t* row_count = p.counters + 64 + row;
+    const int64_t sl = slice_len(p.n), wsl = wave_spill_len(p.n);
+    uint2* region = p.ws + 2 * static_cast<int64_t>(row) * sl;  // part ranges, wave spills
+    uint2* region2 = region + sl;                                 // contiguous frontier
+    uint32_t* counts = reinterpret_cast<uint32_t*>(p.ws + 2 * static_cast<int64_t>(p.m_cap) * sl) +
+                       2 * static_cast<int64_t>(row) * P;
     uint32_t* arrive = p.counters + 64 + p.m_cap + row;
     uint32_t* h0 = sm.hist[0];
     uint32_t* h1 = sm.hist[1];
-    const Frontier A{sm.qa, kCapA, region, &sm.cnt[0]};
-    const Frontier B{sm.qb, kCapB, region2, &sm.cnt[1]};
 
     bool usable = false;
     uint32_t a = 0, nv = 0, q = 0, q1 = 0;
@@ -554,82 +991,188 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
     if (!usable) {
         // No usable view: part 0 runs the exact coarse route over the whole row.
         if (part != 0) return;
-        const uint32_t kq = exact_route(x, L, k, outp, A, h0, h1, sm);
+        WaveFrontier wf{sm.front + wave() * kWaveCap, region + wave() * wsl, 0};
+        const uint32_t kq = exact_route(x, L, k, outp, wf, h0, h1, sm);
+        uint32_t C = 0;
+        bool spill = false;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            C += sm.wcnt[w];
+            spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
+        }
         count_route(p, TOPKF_ROUTE_EXACT_DIRECT);
-        if (*A.cnt > A.cap) count_route(p, TOPKF_ROUTE_SPILL);
-        refine(A, B, h1, h0, kq, outp, k, sm);
+        if (spill) count_route(p, TOPKF_ROUTE_SPILL);
+        finish_waves(C, region, wsl, region2, region, h1, h0, kq, outp, k, sm);
         return;
     }
-    const uint32_t min_seg = static_cast<uint32_t>(p.min_seg);
-    uint32_t Pr = ceil_div(L, min_seg);
+    uint32_t Pr = ceil_div(L, static_cast<uint32_t>(p.min_seg));
     if (Pr > P) Pr = P;
     if (Pr < 1) Pr = 1;
     if (part >= Pr) return;
-    const uint32_t chunk = ceil_div(ceil_div(L, Pr), 4) * 4;
+    const uint32_t chunk = segment_chunk(L, Pr);
     const uint32_t lo = part * chunk < L ? part * chunk : L;
     const uint32_t hi = lo + chunk < L ? lo + chunk : L;
 
-    // Replicated Phase 1: every part derives the same tau0/tau1 from a_r.
-    clear_hist(h0);
-    clear_hist(h1);
-    if (threadIdx.x == 0) { sm.cnt[0] = 0; sm.out_cnt = 0; }
+    // Phases 1 and 2 for this part; the segment's first chunk is in flight
+    // while the (replicated) view is histogrammed.
+    uint32_t T0 = 0, T1 = 0;
+    const Span sp = make_span(x, lo, hi);
+    scan_span<kSegVec>(
+        sp,
+        [&]() {
+            clear_hist(h0);
+            if (threadIdx.x == 0) { sm.cnt[0] = 0; sm.cnt[1] = 0; }
+            __syncthreads();
+            phase1(x, a, nv, S, q, q1, h0, sm);
+            T0 = sm.cut[0];
+            T1 = sm.cut[1];
+        },
+        [&](u32x4 b, uint32_t i0) {
+            uint32_t key[4];
+            bool pp[4], pb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                key[u] = desc_key(b[u]);
+                pp[u] = key[u] <= T0;
+                pb[u] = DUAL && key[u] > T0 && key[u] <= T1;
+            }
+            // kind 0: primary, upward from lo; kind 1: band, downward from hi - 1
+            auto emit = [&](const bool (&pr)[4], int kind) {
+                uint64_t m[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) m[u] = __ballot(pr[u]);
+                const uint64_t any = m[0] | m[1] | m[2] | m[3];
+                if (any == 0) return;
+                uint32_t tot = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) tot += __builtin_popcountll(m[u]);
+                uint32_t base = wave_reserve(&sm.cnt[kind], any, tot);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (pr[u]) {
+                        const uint32_t slot = base + mbcnt(m[u]);
+                        nt_store2(region + (kind ? hi - 1 - slot : lo + slot), i0 + u, key[u]);
+                    }
+                    base += __builtin_popcountll(m[u]);
+                }
+            };
+            emit(pp, 0);
+            if (DUAL) emit(pb, 1);
+        });
     __syncthreads();
-    phase1(x, a, nv, S, q, q1, h0, sm);
-    const uint32_t T0 = sm.cut[0], T1 = sm.cut[1];
-    // Phase 2 over this part's segment; LDS overflow goes to region2 at the
-    // segment's own offset (a segment admits at most hi - lo values).
-    const Frontier Aseg{sm.qa, kCapA, region2 + lo, &sm.cnt[0]};
-    stream_range(x, lo, hi, [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, Aseg, h1); });
-    __syncthreads();
-    const uint32_t nseg = sm.cnt[0];
-    if (threadIdx.x == 0) sm.res[0] = atomicAdd(row_count, nseg);
-    __syncthreads();
-    const uint32_t base = sm.res[0];
-    for (uint32_t e = threadIdx.x; e < nseg; e += kBlock) region[base + e] = fget(Aseg, e);
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) sm.flag = atomicAdd(arrive, 1u) == Pr - 1 ? 1u : 0u;
+    // Publish this part's counts, then arrive; the last arrival finishes.
+    if (threadIdx.x == 0) {
+        counts[2 * part] = sm.cnt[0];
+        counts[2 * part + 1] = sm.cnt[1];
+        __threadfence();  // release this workgroup's range and counts
+        sm.flag = atomicAdd(arrive, 1u) == Pr - 1 ? 1u : 0u;
+        if (sm.flag) {
+            __threadfence();  // acquire every other part's range and counts
+            atomicExch(arrive, 0u);
+        }
+    }
     __syncthreads();
     if (!sm.flag) return;
 
-    // Finisher: the last part to arrive sees every published candidate.
-    __threadfence();
-    uint32_t C = __hip_atomic_load(row_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
+    // ---- finisher: merge the parts (Eq. 27) ----
+    uint32_t cp = 0, cb = 0;
+    if (threadIdx.x < Pr) {
+        cp = counts[2 * threadIdx.x];
+        cb = counts[2 * threadIdx.x + 1];
+    }
+    uint32_t C0 = 0, CB = 0;
+    const uint32_t op = block_excl_scan(cp, &C0, sm);
+    const uint32_t ob = block_excl_scan(cb, &CB, sm);
+    if (threadIdx.x < Pr) { sm.offs[0][threadIdx.x] = op; sm.offs[1][threadIdx.x] = ob; }
     if (threadIdx.x == 0) {
-        __hip_atomic_store(row_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm.cnt[0] = C;
+        sm.offs[0][Pr] = C0;
+        sm.offs[1][Pr] = CB;
         sm.out_cnt = 0;
     }
-    // The merged candidates live only in `region` (a frontier with no LDS part).
-    const Frontier G0{sm.qa, 0, region, &sm.cnt[0]};
     int route = TOPKF_ROUTE_PRIMARY;
-    if (C < k) {
+    uint32_t ctot = C0;
+    if (C0 < k) {
         route = TOPKF_ROUTE_EXACT_UNDERFILL;
-        if (DUAL && T1 > T0) {
-            __syncthreads();
-            stream_range(x, 0, L, [&](u32x4 b, uint32_t i0) { admit4<true>(b, i0, T0, T1, G0, h1); });
-            __syncthreads();
-            C = sm.cnt[0];
-            if (C >= k) route = TOPKF_ROUTE_BAND;
+        if (DUAL && C0 + CB >= k) { route = TOPKF_ROUTE_BAND; ctot = C0 + CB; }
+    }
+    count_route(p, route);
+    if (route == TOPKF_ROUTE_EXACT_UNDERFILL) {
+        WaveFrontier wf{sm.front + wave() * kWaveCap, region + wave() * wsl, 0};
+        const uint32_t kq = exact_route(x, L, k, outp, wf, h0, h1, sm);
+        uint32_t C = 0;
+        bool spill = false;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            C += sm.wcnt[w];
+            spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
+        }
+        if (spill) count_route(p, TOPKF_ROUTE_SPILL);
+        finish_waves(C, region, wsl, region2, region, h1, h0, kq, outp, k, sm);
+        return;
+    }
+    clear_hist(h1);
+    __syncthreads();
+    // Gather the part ranges into one contiguous frontier (LDS, then
+    // region2) and count the leading digit of every candidate.
+    const Frontier G{sm.front, kFront, region2, &sm.cnt[0]};
+    for (uint32_t g0 = 0; g0 < ctot; g0 += 4 * kBlock) {
+        uint2 it[4];
+        bool v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t g = g0 + u * kBlock + threadIdx.x;
+            v[u] = g < ctot;
+            it[u] = make_uint2(0u, kNoElem);
+            if (v[u]) {
+                const int kind = g < C0 ? 0 : 1;
+                const uint32_t r = kind ? g - C0 : g;
+                const uint32_t* off = sm.offs[kind];
+                uint32_t lo_p = 0, hi_p = Pr;  // the part with off[pp] <= r < off[pp + 1]
+                while (hi_p - lo_p > 1) {
+                    const uint32_t mid = (lo_p + hi_p) >> 1;
+                    if (off[mid] <= r) lo_p = mid; else hi_p = mid;
+                }
+                const uint32_t j = r - off[lo_p];
+                const uint32_t s0 = lo_p * chunk;
+                const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
+                const u32x2 t2 = nt_load2(region + (kind ? s1 - 1 - j : s0 + j));
+                it[u] = make_uint2(t2.x, t2.y);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t g = g0 + u * kBlock + threadIdx.x;
+            if (v[u]) {
+                fput(G, g, it[u].x, it[u].y);
+                lds_inc(h1, it[u].y >> 21);
+            }
         }
     }
-    if (C >= k) {
-        // Leading-digit histogram of the merged frontier (Eq. 27).
-        clear_hist(h1);
-        __syncthreads();
-        for (uint32_t e = threadIdx.x; e < C; e += kBlock) lds_inc(h1, region[e].y >> 21);
-        __syncthreads();
-        count_route(p, route);
-        refine(G0, B, h1, h0, k, outp, k, sm);
-    } else {
-        __syncthreads();
-        const uint32_t kq = exact_route(x, L, k, outp, A, h0, h1, sm);
-        count_route(p, route);
-        if (*A.cnt > A.cap) count_route(p, TOPKF_ROUTE_SPILL);
-        refine(A, B, h1, h0, kq, outp, k, sm);
+    if (threadIdx.x == 0) sm.cnt[0] = ctot;
+    __syncthreads();
+    if (ctot > static_cast<uint32_t>(kFront)) count_route(p, TOPKF_ROUTE_SPILL);
+    if (ctot <= static_cast<uint32_t>(kBlock * kRegs)) {
+        refine_regs<kRegs>(
+            [&](int u, uint32_t& i, uint32_t& key) {
+                const uint32_t e = threadIdx.x + kBlock * u;
+                if (e >= ctot) return false;
+                uint2 v;
+                if (e < static_cast<uint32_t>(kFront)) {
+                    v = sm.front[e];
+                } else {
+                    const u32x2 t2 = nt_load2(region2 + (e - kFront));
+                    v = make_uint2(t2.x, t2.y);
+                }
+                i = v.x;
+                key = v.y;
+                return true;
+            },
+            h1, h0, k, 0u, outp, k, sm);
+        return;
     }
+    // General path: Q1 goes to global memory (the part ranges are consumed).
+    const Frontier nxt{sm.front, 0, region, &sm.cnt[1]};
+    refine(G, nxt, h1, h0, k, outp, k, sm);
 }
 
 __global__ void coarse_keys_kernel(const float* x, int64_t n, uint16_t* out) {
@@ -676,7 +1219,7 @@ bool plan_valid(const topkf_plan& pl) {
     if (pl.stride != 0 && pl.stride != 64 && pl.stride != 128) return false;
     if (pl.dual != 0 && pl.dual != 1) return false;
     if (pl.family == TOPKF_FAMILY_PERSISTENT && pl.workers < 1) return false;
-    if (pl.family == TOPKF_FAMILY_KVSPLIT && (pl.splits < 1 || pl.splits > 4096)) return false;
+    if (pl.family == TOPKF_FAMILY_KVSPLIT && (pl.splits < 1 || pl.splits > kMaxSplits)) return false;
     if (pl.family == TOPKF_FAMILY_KVSPLIT && pl.min_segment < 4) return false;
     return true;
 }
@@ -702,6 +1245,7 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         r.family = TOPKF_FAMILY_KVSPLIT;
         int64_t P = (pool + m_cap - 1) / (m_cap > 0 ? m_cap : 1);
         int64_t pmax = (n + r.min_segment - 1) / r.min_segment;
+        if (pmax > kMaxSplits) pmax = kMaxSplits;
         if (P > pmax) P = pmax;
         if (P < 1) P = 1;
         r.splits = static_cast<int32_t>(P);
@@ -713,8 +1257,15 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
 
 void plan_sizes(const topkf_plan& pl, int64_t m_cap, int64_t n, size_t* cb, size_t* wb) {
     *cb = static_cast<size_t>(kCounterHead + 2 * m_cap) * sizeof(uint32_t);
-    const int64_t owners = pl.family == TOPKF_FAMILY_PERSISTENT ? pl.workers : m_cap;
-    *wb = static_cast<size_t>(owners) * 2 * static_cast<size_t>(n) * sizeof(uint2);
+    const size_t per_owner = 2 * static_cast<size_t>(slice_len(n)) * sizeof(uint2);
+    if (pl.family == TOPKF_FAMILY_PERSISTENT) {
+        // two (index, key) slices per worker: wave spills, contiguous frontier
+        *wb = static_cast<size_t>(pl.workers) * per_owner;
+    } else {
+        // per row: part ranges and contiguous frontier, then two counts per part
+        *wb = static_cast<size_t>(m_cap) *
+              (per_owner + 2 * static_cast<size_t>(pl.splits) * sizeof(uint32_t));
+    }
 }
 
 template <int S, bool D>

@@ -88,12 +88,14 @@ def test_workspace_sizes_follow_the_plan():
     pers = topkf.make_plan(topkf.FAMILY_PERSISTENT, 128, 1, workers=10)
     cb, wb = topkf.plan_workspace_size(pers, 77, n)
     assert cb == 4 * (64 + 2 * 77)
-    assert wb == 10 * 2 * n * 8          # two (index, key) spill slices per worker
+    sl = n + 128                         # slice of (index, key) pairs
+    assert wb == 10 * 2 * sl * 8         # two slices per worker
     kv = topkf.make_plan(topkf.FAMILY_KVSPLIT, 64, 0, splits=8)
     cb, wb = topkf.plan_workspace_size(kv, 5, n)
-    assert wb == 5 * 2 * n * 8           # merged candidates + ping-pong per row
+    assert wb == 5 * (2 * sl * 8 + 2 * 8 * 4)  # two slices per row, two counts per part
     for bad in (topkf.make_plan(7, 128), topkf.make_plan(1, 32), topkf.make_plan(1, 64, dual=2),
                 topkf.make_plan(1, 64, workers=0), topkf.make_plan(2, 64, splits=0),
+                topkf.make_plan(2, 64, splits=257),
                 topkf.make_plan(2, 64, splits=2, min_segment=0)):
         with pytest.raises(topkf.TopkfError):
             topkf.plan_workspace_size(bad, 5, n)
