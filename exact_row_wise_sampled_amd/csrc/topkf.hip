@@ -70,13 +70,14 @@ struct Params {
     int32_t k;
     int32_t splits;
     int32_t min_seg;
+    int32_t band_q;  // secondary target K~1 = ceil(band_q * K / 4)
 };
 
 struct alignas(16) Shared {
     uint32_t hist[2][kBins];
     uint2 front[kFront];
     uint32_t offs[2][kMaxSplits + 1];  // KV-split finisher: per-part prefix offsets
-    uint32_t wsum[kWaves];
+    alignas(16) uint32_t wsum[3][kWaves];  // per-wave totals: [0] block_find, [1], [2] scans
     uint32_t wcnt[kWaves];             // wave-private frontier sizes
     uint32_t res[4];
     uint32_t cnt[2];
@@ -130,13 +131,14 @@ __device__ __forceinline__ uint32_t view_phase(uint32_t row, int s) {
 
 __device__ __forceinline__ uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 
-// q = ceil(K~/s) with K~ = ceil(1.5K), q1 with K~1 = ceil(1.75K) (Sec. 4.2;
-// Sec. 6.4 "Conditional rescue").
+// q = ceil(K~/s) with K~ = ceil(1.5K) (Sec. 4.2); q1 = ceil(K~1/s) with
+// K~1 = ceil(band_q * K / 4), 1.75K for band_q = 7 (Sec. 6.4 "Conditional
+// rescue").  Both targets are efficiency knobs only (Sec. 4.6, last para).
 __device__ __forceinline__ uint32_t q_primary(uint32_t k, int s) {
     return ceil_div(ceil_div(3 * k, 2), s);
 }
-__device__ __forceinline__ uint32_t q_secondary(uint32_t k, int s) {
-    return ceil_div(ceil_div(7 * k, 4), s);
+__device__ __forceinline__ uint32_t q_secondary(uint32_t k, int s, int band_q) {
+    return ceil_div(ceil_div(static_cast<uint32_t>(band_q) * k, 4), s);
 }
 
 // ------------------------------------------------------------ wave helpers
@@ -342,6 +344,24 @@ __device__ __forceinline__ void wappend4(const bool (&p)[4], const uint32_t (&id
 
 // ------------------------------------------------------------ block scans
 
+// The sum of the per-wave totals of the waves below this one, and (*all) of
+// all eight, from one broadcast read of the eight totals.
+__device__ __forceinline__ uint32_t waves_below(const uint32_t* wt, uint32_t* all) {
+    const uint4 a = reinterpret_cast<const uint4*>(wt)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(wt)[1];
+    const uint32_t w = wave();
+    uint32_t s = 0;
+    s += w > 0 ? a.x : 0u;
+    s += w > 1 ? a.y : 0u;
+    s += w > 2 ? a.z : 0u;
+    s += w > 3 ? a.w : 0u;
+    s += w > 4 ? b.x : 0u;
+    s += w > 5 ? b.y : 0u;
+    s += w > 6 ? b.z : 0u;
+    *all = a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w;
+    return s;
+}
+
 __device__ __forceinline__ void clear_hist(uint32_t* h) {
     reinterpret_cast<uint4*>(h)[threadIdx.x] = make_uint4(0, 0, 0, 0);
 }
@@ -363,11 +383,10 @@ __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t 
     const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];
     const uint32_t s = v.x + v.y + v.z + v.w;
     const uint32_t incl = wave_incl_scan(s);
-    if (lane() == 63) sm.wsum[wave()] = incl;
+    if (lane() == 63) sm.wsum[0][wave()] = incl;
     __syncthreads();
-    uint32_t base = 0;
-    for (uint32_t w = 0; w < wave(); ++w) base += sm.wsum[w];
-    const uint32_t excl = base + incl - s;
+    uint32_t all;
+    const uint32_t excl = waves_below(sm.wsum[0], &all) + incl - s;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         if (excl < t[i] && t[i] <= excl + s) {
@@ -386,20 +405,15 @@ __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t 
     __syncthreads();
 }
 
-// Exclusive prefix of one value per thread over the block; *total gets the sum.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, Shared& sm) {
+// Exclusive prefix of one value per thread over the block; *total gets the
+// sum.  Uses per-wave total slot `slot` (1 or 2) and one barrier: the next
+// scan on the same slot must be separated from this one by another barrier.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, Shared& sm,
+                                                    int slot) {
     const uint32_t incl = wave_incl_scan(v);
-    if (lane() == 63) sm.wsum[wave()] = incl;
+    if (lane() == 63) sm.wsum[slot][wave()] = incl;
     __syncthreads();
-    uint32_t base = 0, all = 0;
-    for (uint32_t w = 0; w < kWaves; ++w) {
-        const uint32_t ws = sm.wsum[w];
-        if (w < wave()) base += ws;
-        all += ws;
-    }
-    __syncthreads();
-    *total = all;
-    return base + incl - v;
+    return waves_below(sm.wsum[slot], total) + incl - v;
 }
 
 // Sec. 4.3: the inclusive FP32 cutoff of coarse bin tau, as the largest
@@ -604,14 +618,17 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
 }
 
 // Phase 3 (Sec. 4.4) with the whole frontier in registers: each thread holds
-// up to R (index, key) entries given by load(u, idx, key).  hc holds the
-// leading-digit histogram of all entries, kq is the remaining quota and
-// out_base the number of indices committed so far.  Each round finds b_j
-// (Eq. 23), commits the lower digit groups (Eq. 24) and keeps the boundary
-// group (Eq. 25) while counting its next digit; output slots come from block
-// prefix sums.  After the last digit the boundary group holds equal keys and
-// its first `need` entries fill the output.  Commits exactly kq indices.
-template <int R, class Load>
+// up to R (index, key) entries given by load(u, idx, key).  With BUILD_H0 the
+// leading-digit histogram is counted here into hc (cleared and visible);
+// otherwise hc already holds it.  kq is the remaining quota and out_base the
+// number of indices committed before.  Each round finds b_j (Eq. 23),
+// commits the lower digit groups (Eq. 24) and keeps the boundary group
+// (Eq. 25) while counting its next digit; output slots come from block
+// prefix sums and are staged in LDS (the frontier buffer is free once the
+// entries are in registers), then written out with coalesced stores.  After
+// the last digit the boundary group holds equal keys and its first `need`
+// entries fill the output.  Writes out[out_base, k).
+template <int R, bool BUILD_H0, class Load>
 __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t* hn, uint32_t kq,
                                             uint32_t out_base, int32_t* outp, uint32_t k,
                                             Shared& sm) {
@@ -623,6 +640,14 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
         key[u] = kNoElem;
         if (load(u, idx[u], key[u])) act |= 1u << u;
     }
+    if (BUILD_H0) {
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+            if ((act >> u) & 1u) lds_inc(hc, key[u] >> 21);
+    }
+    __syncthreads();  // entries are in registers; the frontier buffer becomes the stage
+    uint32_t* stage = reinterpret_cast<uint32_t*>(sm.front);
+    const uint32_t base0 = out_base;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         if (j < 2) clear_hist(hn);
@@ -648,19 +673,19 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
         const uint32_t ex = block_excl_scan(
             static_cast<uint32_t>(__builtin_popcount(com)) |
                 (static_cast<uint32_t>(__builtin_popcount(tie)) << 16),
-            &tot, sm);
+            &tot, sm, 1);
         const uint32_t tot_c = tot & 0xFFFFu;
         uint32_t pc = out_base + (ex & 0xFFFFu);
         uint32_t pt = ex >> 16;
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             if ((com >> u) & 1u) {
-                if (pc < k) outp[pc] = static_cast<int32_t>(idx[u]);
+                if (pc < k) stage[pc] = idx[u];
                 ++pc;
             }
             if ((tie >> u) & 1u) {
                 const uint32_t slot = out_base + tot_c + pt;
-                if (pt < need && slot < k) outp[slot] = static_cast<int32_t>(idx[u]);
+                if (pt < need && slot < k) stage[slot] = idx[u];
                 ++pt;
             }
         }
@@ -674,6 +699,8 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
         __syncthreads();
         uint32_t* th = hc; hc = hn; hn = th;
     }
+    __syncthreads();
+    for (uint32_t j = base0 + threadIdx.x; j < k; j += kBlock) outp[j] = static_cast<int32_t>(stage[j]);
 }
 
 // Phase 3 (Sec. 4.4), general form: refinement of frontier `cur` whose leading-digit
@@ -806,7 +833,7 @@ __device__ __forceinline__ void finish_waves(uint32_t C, const uint2* spill_base
     if (wmax <= static_cast<uint32_t>(kWaveCap)) {
         const uint32_t mine = sm.wcnt[wave()];
         const uint2* reg = sm.front + wave() * kWaveCap;
-        refine_regs<kWaveRegs>(
+        refine_regs<kWaveRegs, false>(
             [&](int u, uint32_t& i, uint32_t& key) {
                 const uint32_t e = lane() + 64 * u;
                 if (e >= mine) return false;
@@ -861,7 +888,7 @@ __device__ __forceinline__ void select_row(const Params& p, int row, Shared& sm,
     if constexpr (S > 0) {
         uint32_t a;
         const uint32_t nv = view_size<S>(row, L, &a);
-        const uint32_t q = q_primary(k, S), q1 = DUAL ? q_secondary(k, S) : q;
+        const uint32_t q = q_primary(k, S), q1 = DUAL ? q_secondary(k, S, p.band_q) : q;
         if (nv >= q1) {
             uint32_t T0 = 0, T1 = 0;
             const Span sp = make_span(x, 0, L);
@@ -909,29 +936,30 @@ __device__ __forceinline__ void select_row(const Params& p, int row, Shared& sm,
 }
 
 template <int S, bool DUAL>
-__global__ __launch_bounds__(kBlock) void persistent_kernel(Params p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void persistent_kernel(Params p) {
     __shared__ Shared sm;
     const uint32_t G = gridDim.x;
     const int m_live = static_cast<int>(clamp_len(*p.num_valid_rows, p.m_cap));
     uint2* sliceA = p.ws + 2 * static_cast<int64_t>(blockIdx.x) * slice_len(p.n);
     uint2* sliceB = sliceA + slice_len(p.n);
-    int row = blockIdx.x;  // first wave: one row each; then the queue
+    // First wave: workgroup w takes row w; afterwards rows come from the
+    // queue in completion order (Sec. 5.5 "Persistent sampled").  Every
+    // workgroup that took a row draws exactly one ticket that ends its loop,
+    // so a launch draws exactly M_live tickets, 0 .. M_live - 1, in the
+    // queue's modification order.  The draw of ticket M_live - 1 is the last
+    // access of the launch to the queue, and that workgroup returns it to
+    // zero; no other ordering is needed.
+    int row = blockIdx.x;
     while (row < m_live) {
         select_row<S, DUAL>(p, row, sm, sliceA, sliceB);
         __syncthreads();
-        if (threadIdx.x == 0) sm.next_row = static_cast<int32_t>(G + atomicAdd(p.counters, 1u));
+        if (threadIdx.x == 0) {
+            const uint32_t t = atomicAdd(p.counters, 1u);
+            if (t + 1 == static_cast<uint32_t>(m_live)) atomicExch(p.counters, 0u);
+            sm.next_row = static_cast<int32_t>(G + t);
+        }
         __syncthreads();
         row = sm.next_row;
-    }
-    // The last workgroup to leave returns the queue and exit counters to zero.
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t done = atomicAdd(p.counters + 1, 1u);
-        if (done == G - 1) {
-            __threadfence();
-            atomicExch(p.counters, 0u);
-            atomicExch(p.counters + 1, 0u);
-        }
     }
 }
 
@@ -941,17 +969,80 @@ __device__ __forceinline__ uint32_t segment_chunk(uint32_t L, uint32_t Pr) {
     return ceil_div(ceil_div(L, Pr), 4) * 4;
 }
 
-// KV-split mapping (Sec. 4.5, Eqs. 26-27; Sec. 5.5 "Sampled KV-split").
+// KV-split mapping (Sec. 4.5, Eqs. 26-27; Sec. 5.5 "Sampled KV-split"), as
+// two kernels on the same stream.  kvsplit_scan_kernel: P workgroups per row
+// each rebuild the row's view, derive the same tau0/tau1 and scan one
+// contiguous segment, writing the admitted (index, key) pairs into the
+// segment's own range of the row's region (primary candidates upward from
+// the segment start, band candidates T0 < key <= T1 downward from its end)
+// and their two counts.  kvsplit_finish_kernel: one workgroup per row sums
+// the counts (Eq. 27), gathers the candidates into LDS, counts their leading
+// digit and refines.  The kernel boundary makes every part's writes visible
+// to the finisher on any XCD without per-workgroup cache write-back.
 // Workgroups are numbered so that the parts of a row sit on one XCD (the
-// dispatcher deals workgroup ids round-robin over the 8 XCDs), so the
-// replicated view and the finisher's reads stay in that XCD's L2.
-// Each part scans its segment once with the view's tau0/tau1 and writes the
-// admitted (index, key) pairs into its own range of the row's region:
-// primary candidates upward from the segment start, band candidates
-// (T0 < key <= T1) downward from the segment end.  The last part to arrive
-// gathers them into LDS, counts their leading digit and refines.
+// dispatcher deals workgroup ids round-robin over the 8 XCDs), which keeps the
+// replicated view reads in that XCD's L2.
+
+struct RowGeom {
+    uint32_t row, L, a, nv, q, q1, Pr, chunk;
+    bool usable;
+};
+
+// Everything both KV-split kernels derive from (row, ke) alone.
 template <int S, bool DUAL>
-__global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
+__device__ __forceinline__ RowGeom kv_geom(const Params& p, uint32_t row) {
+    RowGeom g{};
+    g.row = row;
+    g.L = clamp_len(p.ke[row], p.n);
+    g.usable = false;
+    if constexpr (S > 0) {
+        g.nv = view_size<S>(row, g.L, &g.a);
+        g.q = q_primary(p.k, S);
+        g.q1 = DUAL ? q_secondary(p.k, S, p.band_q) : g.q;
+        g.usable = g.nv >= g.q1;
+    }
+    uint32_t Pr = ceil_div(g.L > 0 ? g.L : 1u, static_cast<uint32_t>(p.min_seg));
+    const uint32_t P = static_cast<uint32_t>(p.splits);
+    g.Pr = Pr > P ? P : (Pr < 1 ? 1 : Pr);
+    g.chunk = segment_chunk(g.L, g.Pr);
+    return g;
+}
+
+__device__ __forceinline__ uint2* kv_region(const Params& p, uint32_t row) {
+    return p.ws + 2 * static_cast<int64_t>(row) * slice_len(p.n);
+}
+
+__device__ __forceinline__ uint32_t* kv_counts(const Params& p, uint32_t row) {
+    return reinterpret_cast<uint32_t*>(p.ws + 2 * static_cast<int64_t>(p.m_cap) * slice_len(p.n)) +
+           2 * static_cast<int64_t>(row) * p.splits;
+}
+
+// Whole-row exact coarse route by one workgroup (rows without a usable view,
+// and rows whose parts underfill even with the band).
+__device__ __forceinline__ void kv_exact_row(const Params& p, const RowGeom& g, int route,
+                                             Shared& sm) {
+    const uint32_t k = p.k;
+    int32_t* outp = p.out + static_cast<int64_t>(g.row) * k;
+    const float* x = p.logits + static_cast<int64_t>(g.row) * p.stride;
+    uint2* region = kv_region(p, g.row);
+    uint2* region2 = region + slice_len(p.n);
+    const int64_t wsl = wave_spill_len(p.n);
+    WaveFrontier wf{sm.front + wave() * kWaveCap, region + wave() * wsl, 0};
+    const uint32_t kq = exact_route(x, g.L, k, outp, wf, sm.hist[0], sm.hist[1], sm);
+    uint32_t C = 0;
+    bool spill = false;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        C += sm.wcnt[w];
+        spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
+    }
+    count_route(p, route);
+    if (spill) count_route(p, TOPKF_ROUTE_SPILL);
+    finish_waves(C, region, wsl, region2, region, sm.hist[1], sm.hist[0], kq, outp, k, sm);
+}
+
+template <int S, bool DUAL>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvsplit_scan_kernel(Params p) {
     __shared__ Shared sm;
     const uint32_t P = static_cast<uint32_t>(p.splits);
     const uint32_t per_xcd = gridDim.x / 8;
@@ -961,57 +1052,26 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
     const uint32_t m_live = clamp_len(*p.num_valid_rows, p.m_cap);
     if (row >= m_live) return;
     const uint32_t k = p.k;
-    int32_t* outp = p.out + static_cast<int64_t>(row) * k;
-    const uint32_t L = clamp_len(p.ke[row], p.n);
-    if (L <= k) {
+    const RowGeom g = kv_geom<S, DUAL>(p, row);
+    if (g.L <= k) {
         if (part == 0) {
-            sentinel_row(outp, L, k);
+            sentinel_row(p.out + static_cast<int64_t>(row) * k, g.L, k);
             count_route(p, TOPKF_ROUTE_SENTINEL);
         }
         return;
     }
-    const float* x = p.logits + static_cast<int64_t>(row) * p.stride;
-    const int64_t sl = slice_len(p.n), wsl = wave_spill_len(p.n);
-    uint2* region = p.ws + 2 * static_cast<int64_t>(row) * sl;  // part ranges, wave spills
-    uint2* region2 = region + sl;                                 // contiguous frontier
-    uint32_t* counts = reinterpret_cast<uint32_t*>(p.ws + 2 * static_cast<int64_t>(p.m_cap) * sl) +
-                       2 * static_cast<int64_t>(row) * P;
-    uint32_t* arrive = p.counters + 64 + p.m_cap + row;
-    uint32_t* h0 = sm.hist[0];
-    uint32_t* h1 = sm.hist[1];
-
-    bool usable = false;
-    uint32_t a = 0, nv = 0, q = 0, q1 = 0;
-    if constexpr (S > 0) {
-        nv = view_size<S>(row, L, &a);
-        q = q_primary(k, S);
-        q1 = DUAL ? q_secondary(k, S) : q;
-        usable = nv >= q1;
-    }
-    if (!usable) {
+    if (!g.usable) {
         // No usable view: part 0 runs the exact coarse route over the whole row.
-        if (part != 0) return;
-        WaveFrontier wf{sm.front + wave() * kWaveCap, region + wave() * wsl, 0};
-        const uint32_t kq = exact_route(x, L, k, outp, wf, h0, h1, sm);
-        uint32_t C = 0;
-        bool spill = false;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            C += sm.wcnt[w];
-            spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
-        }
-        count_route(p, TOPKF_ROUTE_EXACT_DIRECT);
-        if (spill) count_route(p, TOPKF_ROUTE_SPILL);
-        finish_waves(C, region, wsl, region2, region, h1, h0, kq, outp, k, sm);
+        if (part == 0) kv_exact_row(p, g, TOPKF_ROUTE_EXACT_DIRECT, sm);
         return;
     }
-    uint32_t Pr = ceil_div(L, static_cast<uint32_t>(p.min_seg));
-    if (Pr > P) Pr = P;
-    if (Pr < 1) Pr = 1;
-    if (part >= Pr) return;
-    const uint32_t chunk = segment_chunk(L, Pr);
-    const uint32_t lo = part * chunk < L ? part * chunk : L;
-    const uint32_t hi = lo + chunk < L ? lo + chunk : L;
+    if (part >= g.Pr) return;
+    const uint32_t L = g.L;
+    const uint32_t lo = part * g.chunk < L ? part * g.chunk : L;
+    const uint32_t hi = lo + g.chunk < L ? lo + g.chunk : L;
+    const float* x = p.logits + static_cast<int64_t>(row) * p.stride;
+    uint2* region = kv_region(p, row);
+    uint32_t* h0 = sm.hist[0];
 
     // Phases 1 and 2 for this part; the segment's first chunk is in flight
     // while the (replicated) view is histogrammed.
@@ -1023,7 +1083,7 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
             clear_hist(h0);
             if (threadIdx.x == 0) { sm.cnt[0] = 0; sm.cnt[1] = 0; }
             __syncthreads();
-            phase1(x, a, nv, S, q, q1, h0, sm);
+            phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm);
             T0 = sm.cut[0];
             T1 = sm.cut[1];
         },
@@ -1060,29 +1120,43 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
             if (DUAL) emit(pb, 1);
         });
     __syncthreads();
-    // Publish this part's counts, then arrive; the last arrival finishes.
     if (threadIdx.x == 0) {
+        uint32_t* counts = kv_counts(p, row);
         counts[2 * part] = sm.cnt[0];
         counts[2 * part + 1] = sm.cnt[1];
-        __threadfence();  // release this workgroup's range and counts
-        sm.flag = atomicAdd(arrive, 1u) == Pr - 1 ? 1u : 0u;
-        if (sm.flag) {
-            __threadfence();  // acquire every other part's range and counts
-            atomicExch(arrive, 0u);
-        }
     }
-    __syncthreads();
-    if (!sm.flag) return;
+}
 
-    // ---- finisher: merge the parts (Eq. 27) ----
+template <int S, bool DUAL>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvsplit_finish_kernel(Params p) {
+    __shared__ Shared sm;
+    // same XCD as the row's parts in kvsplit_scan_kernel
+    const uint32_t per_xcd = gridDim.x / 8;
+    const uint32_t row = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (row >= static_cast<uint32_t>(p.m_cap)) return;
+    const uint32_t m_live = clamp_len(*p.num_valid_rows, p.m_cap);
+    if (row >= m_live) return;
+    const uint32_t k = p.k;
+    const RowGeom g = kv_geom<S, DUAL>(p, row);
+    if (g.L <= k || !g.usable) return;  // finished by the scan kernel
+    const uint32_t L = g.L, Pr = g.Pr, chunk = g.chunk;
+    int32_t* outp = p.out + static_cast<int64_t>(row) * k;
+    uint2* region = kv_region(p, row);
+    uint2* region2 = region + slice_len(p.n);
+    const uint32_t* counts = kv_counts(p, row);
+    uint32_t* h0 = sm.hist[0];
+    uint32_t* h1 = sm.hist[1];
+
+    // Merge the parts (Eq. 27): prefix offsets of the primary and band counts.
     uint32_t cp = 0, cb = 0;
     if (threadIdx.x < Pr) {
         cp = counts[2 * threadIdx.x];
         cb = counts[2 * threadIdx.x + 1];
     }
+    clear_hist(h1);
     uint32_t C0 = 0, CB = 0;
-    const uint32_t op = block_excl_scan(cp, &C0, sm);
-    const uint32_t ob = block_excl_scan(cb, &CB, sm);
+    const uint32_t op = block_excl_scan(cp, &C0, sm, 1);
+    const uint32_t ob = block_excl_scan(cb, &CB, sm, 2);
     if (threadIdx.x < Pr) { sm.offs[0][threadIdx.x] = op; sm.offs[1][threadIdx.x] = ob; }
     if (threadIdx.x == 0) {
         sm.offs[0][Pr] = C0;
@@ -1095,37 +1169,69 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
         route = TOPKF_ROUTE_EXACT_UNDERFILL;
         if (DUAL && C0 + CB >= k) { route = TOPKF_ROUTE_BAND; ctot = C0 + CB; }
     }
-    count_route(p, route);
     if (route == TOPKF_ROUTE_EXACT_UNDERFILL) {
-        WaveFrontier wf{sm.front + wave() * kWaveCap, region + wave() * wsl, 0};
-        const uint32_t kq = exact_route(x, L, k, outp, wf, h0, h1, sm);
-        uint32_t C = 0;
-        bool spill = false;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            C += sm.wcnt[w];
-            spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
-        }
-        if (spill) count_route(p, TOPKF_ROUTE_SPILL);
-        finish_waves(C, region, wsl, region2, region, h1, h0, kq, outp, k, sm);
+        kv_exact_row(p, g, route, sm);
         return;
     }
-    clear_hist(h1);
-    __syncthreads();
-    // Gather the part ranges into one contiguous frontier (LDS, then
-    // region2) and count the leading digit of every candidate.
+    count_route(p, route);
+    __syncthreads();  // offsets visible
+    if (ctot <= static_cast<uint32_t>(kBlock * kRegs)) {
+        // Each thread locates its candidates (the part p with off[p] <= r <
+        // off[p + 1]) with a branch-free binary search, all kRegs at once, and
+        // loads them straight into registers.
+        uint32_t src[kRegs];
+        uint32_t pstep = 1;
+        while (pstep * 2 <= Pr) pstep *= 2;
+#pragma unroll
+        for (int u = 0; u < kRegs; ++u) src[u] = 0;
+        for (uint32_t step = pstep; step > 0; step >>= 1) {
+#pragma unroll
+            for (int u = 0; u < kRegs; ++u) {
+                const uint32_t gi = threadIdx.x + kBlock * u;
+                const int kind = gi < C0 ? 0 : 1;
+                const uint32_t r = kind ? gi - C0 : gi;
+                const uint32_t cand = src[u] + step;
+                if (gi < ctot && cand < Pr && sm.offs[kind][cand] <= r) src[u] = cand;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRegs; ++u) {
+            const uint32_t gi = threadIdx.x + kBlock * u;
+            const int kind = gi < C0 ? 0 : 1;
+            const uint32_t r = kind ? gi - C0 : gi;
+            const uint32_t pp = src[u];
+            const uint32_t j = gi < ctot ? r - sm.offs[kind][pp] : 0;
+            const uint32_t s0 = pp * chunk;
+            const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
+            src[u] = kind ? s1 - 1 - j : s0 + j;
+        }
+        refine_regs<kRegs, true>(
+            [&](int u, uint32_t& i, uint32_t& key) {
+                const uint32_t gi = threadIdx.x + kBlock * u;
+                if (gi >= ctot) return false;
+                const u32x2 t2 = nt_load2(region + src[u]);
+                i = t2.x;
+                key = t2.y;
+                return true;
+            },
+            h1, h0, k, 0u, outp, k, sm);
+        return;
+    }
+    // Large frontier: gather the part ranges into one contiguous frontier
+    // (LDS, then region2), count the leading digit, refine through ping-pong
+    // buffers.
     const Frontier G{sm.front, kFront, region2, &sm.cnt[0]};
     for (uint32_t g0 = 0; g0 < ctot; g0 += 4 * kBlock) {
         uint2 it[4];
         bool v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const uint32_t g = g0 + u * kBlock + threadIdx.x;
-            v[u] = g < ctot;
+            const uint32_t gi = g0 + u * kBlock + threadIdx.x;
+            v[u] = gi < ctot;
             it[u] = make_uint2(0u, kNoElem);
             if (v[u]) {
-                const int kind = g < C0 ? 0 : 1;
-                const uint32_t r = kind ? g - C0 : g;
+                const int kind = gi < C0 ? 0 : 1;
+                const uint32_t r = kind ? gi - C0 : gi;
                 const uint32_t* off = sm.offs[kind];
                 uint32_t lo_p = 0, hi_p = Pr;  // the part with off[pp] <= r < off[pp + 1]
                 while (hi_p - lo_p > 1) {
@@ -1141,35 +1247,16 @@ __global__ __launch_bounds__(kBlock) void kvsplit_kernel(Params p) {
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const uint32_t g = g0 + u * kBlock + threadIdx.x;
+            const uint32_t gi = g0 + u * kBlock + threadIdx.x;
             if (v[u]) {
-                fput(G, g, it[u].x, it[u].y);
+                fput(G, gi, it[u].x, it[u].y);
                 lds_inc(h1, it[u].y >> 21);
             }
         }
     }
     if (threadIdx.x == 0) sm.cnt[0] = ctot;
     __syncthreads();
-    if (ctot > static_cast<uint32_t>(kFront)) count_route(p, TOPKF_ROUTE_SPILL);
-    if (ctot <= static_cast<uint32_t>(kBlock * kRegs)) {
-        refine_regs<kRegs>(
-            [&](int u, uint32_t& i, uint32_t& key) {
-                const uint32_t e = threadIdx.x + kBlock * u;
-                if (e >= ctot) return false;
-                uint2 v;
-                if (e < static_cast<uint32_t>(kFront)) {
-                    v = sm.front[e];
-                } else {
-                    const u32x2 t2 = nt_load2(region2 + (e - kFront));
-                    v = make_uint2(t2.x, t2.y);
-                }
-                i = v.x;
-                key = v.y;
-                return true;
-            },
-            h1, h0, k, 0u, outp, k, sm);
-        return;
-    }
+    count_route(p, TOPKF_ROUTE_SPILL);
     // General path: Q1 goes to global memory (the part ranges are consumed).
     const Frontier nxt{sm.front, 0, region, &sm.cnt[1]};
     refine(G, nxt, h1, h0, k, outp, k, sm);
@@ -1221,6 +1308,7 @@ bool plan_valid(const topkf_plan& pl) {
     if (pl.family == TOPKF_FAMILY_PERSISTENT && pl.workers < 1) return false;
     if (pl.family == TOPKF_FAMILY_KVSPLIT && (pl.splits < 1 || pl.splits > kMaxSplits)) return false;
     if (pl.family == TOPKF_FAMILY_KVSPLIT && pl.min_segment < 4) return false;
+    if (pl.dual && (pl.band_quarters < 7 || pl.band_quarters > 32)) return false;
     return true;
 }
 
@@ -1236,6 +1324,7 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
     else r.stride = 128;
     r.dual = r.stride ? 1 : 0;
     r.min_segment = 8192;
+    r.band_quarters = 7;
     const int64_t pool = static_cast<int64_t>(cus) * occupancy;
     if (r.stride == 0 || m_cap >= pool) {
         r.family = TOPKF_FAMILY_PERSISTENT;
@@ -1250,6 +1339,9 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         if (P < 1) P = 1;
         r.splits = static_cast<int32_t>(P);
         r.workers = 1;
+        // The parts collect the band in the same pass, so a deeper secondary
+        // target costs little and keeps whole-row exact recovery rare.
+        r.band_quarters = 10;
     }
     *pl = r;
     return TOPKF_OK;
@@ -1275,8 +1367,13 @@ hipError_t launch_family(const topkf_plan& pl, const Params& prm, hipStream_t st
     } else {
         const int64_t total = static_cast<int64_t>(prm.m_cap) * pl.splits;
         const int64_t per_xcd = (total + 7) / 8;
-        hipLaunchKernelGGL((kvsplit_kernel<S, D>), dim3(static_cast<uint32_t>(per_xcd * 8)),
+        hipLaunchKernelGGL((kvsplit_scan_kernel<S, D>), dim3(static_cast<uint32_t>(per_xcd * 8)),
                            dim3(kBlock), 0, st, prm);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t rows_per_xcd = (static_cast<int64_t>(prm.m_cap) + 7) / 8;
+        hipLaunchKernelGGL((kvsplit_finish_kernel<S, D>),
+                           dim3(static_cast<uint32_t>(rows_per_xcd * 8)), dim3(kBlock), 0, st, prm);
     }
     return hipGetLastError();
 }
@@ -1318,6 +1415,7 @@ topkf_status run(const float* logits, int64_t m_cap, int64_t n, int64_t stride,
     prm.k = top_k;
     prm.splits = pl.splits;
     prm.min_seg = pl.min_segment;
+    prm.band_q = pl.band_quarters;
     hipError_t e;
     switch (pl.stride * 2 + pl.dual) {
         case 0: case 1: e = launch_family<0, false>(pl, prm, st); break;

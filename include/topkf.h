@@ -127,6 +127,9 @@ typedef struct {
     int32_t workers;  /* persistent: workgroups in the pool (>= 1) */
     int32_t min_segment; /* KV-split: shortest segment in elements; a row of
                             length L uses min(P, ceil(L / min_segment)) parts */
+    int32_t band_quarters; /* secondary target K~1 = ceil(band_quarters * K / 4),
+                              7..32 when dual (paper Sec. 6.4 uses 1.75K, i.e. 7);
+                              ignored without dual */
 } topkf_plan;
 
 /*
