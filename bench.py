@@ -53,6 +53,44 @@ def algorithmic_bytes(ke, n: int, k: int, stride: int) -> int:
     return total
 
 
+def measured_traffic(config: str):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (profiles/hbm_traffic.json, calibrated against a plain device copy), or None
+    when they were taken on a different kernel source than the one built here."""
+    import hashlib
+    src = os.path.join(ROOT, "exact_row_wise_sampled_amd", "csrc", "topkf.hip")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != digest:
+        return None
+    cfg = rec.get("configs", {}).get(config)
+    return None if cfg is None else int(cfg["traffic_bytes"])
+
+
+def stream_read_reference(dev, nbytes: int = 1 << 30) -> float:
+    """GB/s of a plain library reduction that reads nbytes once (context for the
+    fraction of achievable bandwidth)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        x.sum()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del x
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(w, seconds: float) -> dict:
     """The CPU oracle (complete sort per row, threaded over rows) on the same batch."""
     from oracle import oracle
@@ -81,6 +119,13 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=5.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call directly instead of replaying a HIP graph "
+                         "(for hardware-counter runs)")
+    ap.add_argument("--no-ref", action="store_true", help="skip the streaming-read reference")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 256 MiB device copy first, the calibration "
+                         "reference for FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selector has no multi-GPU path "
@@ -93,6 +138,12 @@ def main() -> int:
     from exact_row_wise_sampled_amd import topkf, workloads
 
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = workloads.make(args.config)
     m, n, k = w.m, w.n, w.k
     plan = topkf.plan_for(m, n, torch.cuda.get_device_properties(dev).multi_processor_count)
@@ -120,23 +171,30 @@ def main() -> int:
 
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
+
+    def one_pass():
         for i in range(copies):
             sel(xs[i], ke, outs[i], nvr, k, stream=stream)
+
+    with torch.cuda.stream(stream):
+        one_pass()
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(copies):
-            sel(xs[i], ke, outs[i], nvr, k, stream=stream)
-    torch.cuda.synchronize()
+    if args.eager:
+        replay = one_pass
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            one_pass()
+        torch.cuda.synchronize()
+        replay = graph.replay
 
     reps_warm = max(1, math.ceil(args.warmup / copies))
     reps = max(1, math.ceil(args.steps / copies))
     steps = reps * copies
     with torch.cuda.stream(stream):
         for _ in range(reps_warm):
-            graph.replay()
+            replay()
     torch.cuda.synchronize()
     if int(sel.counters.sum().item()) != 0:
         print("bench: counters not zero after replays", file=sys.stderr)
@@ -148,7 +206,7 @@ def main() -> int:
     with torch.cuda.stream(stream):
         ev0.record(stream)
         for _ in range(reps):
-            graph.replay()
+            replay()
         ev1.record(stream)
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
@@ -158,6 +216,11 @@ def main() -> int:
     gbs = score_bytes / (ms_step * 1e-3) / 1e9
     alg = algorithmic_bytes(w.ke, n, k, plan.stride)
     achieved = alg / (ms_step * 1e-3) / 1e9
+    kernels = (["persistent_kernel<%d,%s>" % (plan.stride, "true" if plan.dual else "false")]
+               if plan.family == 1 else
+               ["kvsplit_scan_kernel<%d,%s>" % (plan.stride, "true" if plan.dual else "false"),
+                "kvsplit_finish_kernel<%d,%s>" % (plan.stride, "true" if plan.dual else "false")])
+    traffic = measured_traffic(args.config)
     line = {
         "metric": "score-row GB/s and rows/s vs HBM peak, K=2048, ragged rows up to 512K",
         "value": round(gbs, 2),
@@ -178,9 +241,15 @@ def main() -> int:
                    "plan": plan.as_dict()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": alg,
-                     "kernel": "persistent_kernel" if plan.family == 1 else "kvsplit_kernel"},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": alg,
+                     "kernels": kernels,
+                     "timing": "achieved = algorithmic bytes / ms_per_step; one call runs "
+                               "every listed kernel"},
     }
+    if not args.no_ref:
+        ref = stream_read_reference(dev)
+        line["stream_read_ref_gbs"] = round(ref, 1)
+        line["stream_read_ref_frac"] = round(gbs / ref, 4)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -114,7 +114,8 @@ const char* topkf_status_string(topkf_status status);
 /* Kernel families (paper Sec. 5.5, Fig. 6). */
 #define TOPKF_FAMILY_AUTO 0
 #define TOPKF_FAMILY_PERSISTENT 1 /* one 512-thread workgroup owns a row; rows from a queue */
-#define TOPKF_FAMILY_KVSPLIT 2    /* P workgroups split one row; last arrival finishes */
+#define TOPKF_FAMILY_KVSPLIT 2    /* P workgroups scan segments of a row, then one
+                                     workgroup per row merges and refines */
 
 typedef struct {
     int32_t family;   /* TOPKF_FAMILY_* */
