@@ -46,6 +46,8 @@ constexpr int kCapA = 4096;                  // general path: LDS part of Q1 / Q
 constexpr int kRowVec = 4;      // persistent scan: 128-bit loads per thread per chunk
 constexpr int kSegVec = 8;      // KV-split scan: 128-bit loads per thread per chunk
 constexpr int kSampleVec = 8;   // view samples per thread per batch
+constexpr int kLookVec = 2;     // next-row view samples per thread held across a chunk
+constexpr uint32_t kLookMaxView = 65535;  // packed 16-bit lookahead bins
 constexpr int kMaxSplits = 256; // KV-split parts per row
 // A NaN pattern whose descending key is 0xFFFFFFFF: larger than every cutoff,
 // so it marks lanes that hold no element.
@@ -75,6 +77,7 @@ struct Params {
 
 struct alignas(16) Shared {
     uint32_t hist[2][kBins];
+    uint32_t look[kBins / 2];  // persistent: next row's view histogram, two 16-bit bins a word
     uint2 front[kFront];
     uint32_t offs[2][kMaxSplits + 1];  // KV-split finisher: per-part prefix offsets
     alignas(16) uint32_t wsum[3][kWaves];  // per-wave totals: [0] block_find, [1], [2] scans
@@ -86,6 +89,7 @@ struct alignas(16) Shared {
     uint32_t cut[2];
     int32_t next_row;
     uint32_t flag;
+    uint32_t kext[2];  // KV-split finisher: smallest and largest candidate key
 };
 static_assert(sizeof(Shared) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
@@ -165,6 +169,51 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xA, 0xF, false));
     x += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xC, 0xF, false));
     return x;
+}
+
+// Minimum / maximum of x over the wave (wave-uniform), by the same DPP steps.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_min(uint32_t x) {
+    const uint32_t y = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(-1, static_cast<int>(x), CTRL, ROW_MASK, 0xF, false));
+    return y < x ? y : x;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t x) {
+    const uint32_t y = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK, 0xF, false));
+    return y > x ? y : x;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+    x = dpp_min<0x111, 0xF>(x);
+    x = dpp_min<0x112, 0xF>(x);
+    x = dpp_min<0x114, 0xF>(x);
+    x = dpp_min<0x118, 0xF>(x);
+    x = dpp_min<0x142, 0xA>(x);
+    x = dpp_min<0x143, 0xC>(x);
+    return readlane(x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    x = dpp_max<0x111, 0xF>(x);
+    x = dpp_max<0x112, 0xF>(x);
+    x = dpp_max<0x114, 0xF>(x);
+    x = dpp_max<0x118, 0xF>(x);
+    x = dpp_max<0x142, 0xA>(x);
+    x = dpp_max<0x143, 0xC>(x);
+    return readlane(x, 63);
+}
+
+// Folds this wave's minimum of mn and maximum of mx into LDS.
+__device__ __forceinline__ void lds_extremes(uint32_t* e, uint32_t mn, uint32_t mx) {
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane() == 0) {
+        __hip_atomic_fetch_min(e, mn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_max(e + 1, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
 }
 
 // One LDS reservation for the lanes in m; returns the first reserved slot.
@@ -332,6 +381,17 @@ __device__ __forceinline__ void wappend4(const bool (&p)[4], const uint32_t (&id
     uint32_t base = f.n;
 #pragma unroll
     for (int u = 0; u < 4; ++u) f.n += __builtin_popcountll(m[u]);
+    if (f.n <= static_cast<uint32_t>(kWaveCap)) {  // wave-uniform: every new slot is in LDS
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (p[u]) {
+                f.lds[base + mbcnt(m[u])] = make_uint2(idx[u], key[u]);
+                lds_inc(h, bin[u]);
+            }
+            base += __builtin_popcountll(m[u]);
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         if (p[u]) {
@@ -366,11 +426,22 @@ __device__ __forceinline__ void clear_hist(uint32_t* h) {
     reinterpret_cast<uint4*>(h)[threadIdx.x] = make_uint4(0, 0, 0, 0);
 }
 
+__device__ __forceinline__ void clear_look(uint32_t* h) {
+    reinterpret_cast<uint2*>(h)[threadIdx.x] = make_uint2(0, 0);
+}
+
+// Adds one to 16-bit bin `bin` of a packed histogram (two bins per word; a
+// bin never exceeds kLookMaxView, so no carry crosses into the neighbour).
+__device__ __forceinline__ void look_inc(uint32_t* h, uint32_t bin) {
+    atomicAdd(h + (bin >> 1), 1u << ((bin & 1u) << 4));
+}
+
 // For each target t[i] (1 <= t[i] <= sum of hist), finds b = min{b : H(b) >=
 // t[i]} and H(b - 1) (Eqs. 15, 23), written to sm.res[2i], sm.res[2i + 1].
 // Each thread owns 4 consecutive bins.  Reads hist before its first barrier
 // and ends with a barrier, so hist may be rewritten right after it returns.
-template <int NT>
+// PACKED: hist holds two 16-bit bins per word (the lookahead histogram).
+template <int NT, bool PACKED = false>
 __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t (&t)[NT], Shared& sm) {
     const uint32_t tid = threadIdx.x;
     // Defaults keep every later LDS index in range should a target exceed
@@ -380,7 +451,13 @@ __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t 
 #pragma unroll
         for (int i = 0; i < NT; ++i) { sm.res[2 * i] = kBins - 1; sm.res[2 * i + 1] = 0; }
     }
-    const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];
+    uint4 v;
+    if (PACKED) {
+        const uint2 w = reinterpret_cast<const uint2*>(hist)[tid];
+        v = make_uint4(w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16);
+    } else {
+        v = reinterpret_cast<const uint4*>(hist)[tid];
+    }
     const uint32_t s = v.x + v.y + v.z + v.w;
     const uint32_t incl = wave_incl_scan(s);
     if (lane() == 63) sm.wsum[0][wave()] = incl;
@@ -466,11 +543,16 @@ __device__ __forceinline__ Span make_span(const float* x, uint32_t lo, uint32_t 
 
 template <int U>
 __device__ __forceinline__ void load_chunk(const Span& sp, uint32_t base, u32x4 (&v)[U]) {
-    const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo);
+    const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo) + base + threadIdx.x;
+    if (base + U * kBlock <= sp.nvec) {  // a whole chunk inside the span: no per-lane bounds
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(xv + u * kBlock);
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t vi = base + u * kBlock + threadIdx.x;
-        if (vi < sp.nvec) v[u] = __builtin_nontemporal_load(xv + vi);
+        if (vi < sp.nvec) v[u] = __builtin_nontemporal_load(xv + u * kBlock);
         else v[u] = u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
     }
 }
@@ -479,9 +561,11 @@ __device__ __forceinline__ void load_chunk(const Span& sp, uint32_t base, u32x4 
 // first chunk (U vectors per thread) and the head/tail elements loaded before
 // pre() runs, so their latency overlaps pre().  Later chunks are double
 // buffered: the next chunk is in flight while the current one is processed.
+// mid() runs exactly once, after the first chunk (or after the head/tail
+// elements when there is no chunk), with the second chunk already in flight.
 // Every thread of the block must call it with the same span.
-template <int U, class Pre, class F>
-__device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f) {
+template <int U, class Pre, class F, class Mid>
+__device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f, Mid&& mid) {
     const uint32_t tid = threadIdx.x;
     u32x4 cur[U];
     if (sp.nvec) load_chunk<U>(sp, 0, cur);
@@ -496,16 +580,23 @@ __device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f) {
         if (more) load_chunk<U>(sp, base + kBlock * U, nxt);
 #pragma unroll
         for (int u = 0; u < U; ++u) f(cur[u], sp.vlo + 4 * (base + u * kBlock + tid));
+        if (base == 0) mid();
         if (more) {
 #pragma unroll
             for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
     }
+    if (sp.nvec == 0) mid();
 }
 
 struct NoPre {
     __device__ void operator()() const {}
 };
+
+template <int U, class Pre, class F>
+__device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f) {
+    scan_span<U>(sp, pre, f, NoPre{});
+}
 
 // Phase 2 admission of one 4-element group: key <= hi (and key > lo for the
 // band of Eq. 18), appended to the wave frontier with its leading digit
@@ -864,18 +955,45 @@ __device__ __forceinline__ uint32_t clamp_len(int32_t v, int32_t n) {
     return static_cast<uint32_t>(v < 0 ? 0 : (v > n ? n : v));
 }
 
-// One row, whole-row ownership (persistent mapping).  sliceA holds the wave
-// spills, sliceB is the contiguous frontier of the general path.
+// The row a persistent worker takes next, its valid length and whether its
+// view histogram already sits in sm.look (its Phase 1 ran ahead).
+struct NextRow {
+    int row;
+    uint32_t L;
+    bool looked;
+};
+
+// Ticket of the persistent queue (Sec. 5.5 "Persistent sampled").  A launch
+// draws exactly M_live tickets, 0 .. M_live - 1, in the queue's modification
+// order: every row taken draws one, and the one drawn for a workgroup's last
+// row ends its loop.  The draw of ticket M_live - 1 is therefore the last
+// access of the launch to the queue, and that workgroup returns it to zero; no
+// other ordering is needed.  Thread 0 only.
+__device__ __forceinline__ int publish_ticket(const Params& p, uint32_t t, int m_live, Shared& sm) {
+    if (t + 1 == static_cast<uint32_t>(m_live)) atomicExch(p.counters, 0u);
+    const int rn = static_cast<int>(gridDim.x + t);
+    sm.next_row = rn;
+    return rn;
+}
+
+// One row, whole-row ownership (persistent mapping).  L is the row's valid
+// length; `looked`: sm.look holds the row's view histogram.  Thread 0 holds
+// ticket t, drawn when the row started.  sliceA holds the wave spills, sliceB
+// is the contiguous frontier of the general path.  On the sampled route the
+// next row is published during Phase 1, and that row's view samples are
+// gathered into sm.look while this row's Phase 2 streams (its Phase 1 runs
+// ahead); nr.row < 0 means the next row is not known yet.
 template <int S, bool DUAL>
-__device__ __forceinline__ void select_row(const Params& p, int row, Shared& sm, uint2* sliceA,
-                                           uint2* sliceB) {
+__device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t L, bool looked,
+                                              uint32_t t, int m_live, Shared& sm, uint2* sliceA,
+                                              uint2* sliceB) {
     const uint32_t k = p.k;
+    NextRow nr{-1, 0, false};
     int32_t* outp = p.out + static_cast<int64_t>(row) * k;
-    const uint32_t L = clamp_len(p.ke[row], p.n);
     if (L <= k) {
         sentinel_row(outp, L, k);
         count_route(p, TOPKF_ROUTE_SENTINEL);
-        return;
+        return nr;
     }
     const float* x = p.logits + static_cast<int64_t>(row) * p.stride;
     const int64_t wsl = wave_spill_len(p.n);
@@ -891,19 +1009,73 @@ __device__ __forceinline__ void select_row(const Params& p, int row, Shared& sm,
         const uint32_t q = q_primary(k, S), q1 = DUAL ? q_secondary(k, S, p.band_q) : q;
         if (nv >= q1) {
             uint32_t T0 = 0, T1 = 0;
+            int32_t ke_next = 0;
+            uint32_t na = 0, nnv = 0;
+            const float* xn = nullptr;
+            bool on = false;
+            uint32_t nb[kLookVec];
             const Span sp = make_span(x, 0, L);
             scan_span<kRowVec>(
                 sp,
                 [&]() {
-                    clear_hist(h0);
                     clear_hist(h1);
-                    if (threadIdx.x == 0) sm.out_cnt = 0;
-                    __syncthreads();
-                    phase1(x, a, nv, S, q, q1, h0, sm);
+                    if (threadIdx.x == 0) {
+                        sm.out_cnt = 0;
+                        publish_ticket(p, t, m_live, sm);
+                    }
+                    if (looked) {
+                        const uint32_t tg[2] = {q, q1};
+                        block_find<2, true>(sm.look, tg, sm);
+                        clear_look(sm.look);
+                        if (wave() < 2) {
+                            const uint32_t c = wave_cutoff(sm.res[2 * wave()]);
+                            if (lane() == 0) sm.cut[wave()] = c;
+                        }
+                        __syncthreads();
+                    } else {
+                        clear_hist(h0);
+                        clear_look(sm.look);
+                        __syncthreads();
+                        phase1(x, a, nv, S, q, q1, h0, sm);
+                    }
                     T0 = sm.cut[0];
                     T1 = sm.cut[1];
+                    nr.row = sm.next_row;
+                    if (nr.row < m_live) ke_next = p.ke[nr.row];
                 },
-                [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, wf, h1); });
+                [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, wf, h1); },
+                [&]() {
+                    // The next row's geometry and first sample batch, in flight
+                    // while the rest of this row streams.
+                    nr.L = nr.row < m_live ? clamp_len(ke_next, p.n) : 0u;
+                    if (nr.L > k) {
+                        nnv = view_size<S>(static_cast<uint32_t>(nr.row), nr.L, &na);
+                        on = nnv >= q1 && nnv <= kLookMaxView;
+                        xn = p.logits + static_cast<int64_t>(nr.row) * p.stride;
+                    }
+#pragma unroll
+                    for (int u = 0; u < kLookVec; ++u) {
+                        const uint32_t j = u * kBlock + threadIdx.x;
+                        nb[u] = on && j < nnv ? __float_as_uint(xn[na + j * S]) : kNoElem;
+                    }
+                });
+            if (on) {
+#pragma unroll
+                for (int u = 0; u < kLookVec; ++u)
+                    if (nb[u] != kNoElem) look_inc(sm.look, coarse_of_bits(nb[u]));
+                for (uint32_t j0 = kBlock * kLookVec; j0 < nnv; j0 += kBlock * kSampleVec) {
+                    uint32_t b[kSampleVec];
+#pragma unroll
+                    for (int u = 0; u < kSampleVec; ++u) {
+                        const uint32_t j = j0 + u * kBlock + threadIdx.x;
+                        b[u] = j < nnv ? __float_as_uint(xn[na + j * S]) : kNoElem;
+                    }
+#pragma unroll
+                    for (int u = 0; u < kSampleVec; ++u)
+                        if (b[u] != kNoElem) look_inc(sm.look, coarse_of_bits(b[u]));
+                }
+            }
+            nr.looked = on;
             C = publish_waves(wf, sm);
             route = TOPKF_ROUTE_PRIMARY;
             if (C < k) {
@@ -933,33 +1105,36 @@ __device__ __forceinline__ void select_row(const Params& p, int row, Shared& sm,
     for (int w = 0; w < kWaves; ++w) spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
     if (spill) count_route(p, TOPKF_ROUTE_SPILL);
     finish_waves(C, sliceA, wsl, sliceB, sliceA, h1, h0, kq, outp, k, sm);
+    return nr;
 }
 
 template <int S, bool DUAL>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void persistent_kernel(Params p) {
     __shared__ Shared sm;
-    const uint32_t G = gridDim.x;
     const int m_live = static_cast<int>(clamp_len(*p.num_valid_rows, p.m_cap));
     uint2* sliceA = p.ws + 2 * static_cast<int64_t>(blockIdx.x) * slice_len(p.n);
     uint2* sliceB = sliceA + slice_len(p.n);
     // First wave: workgroup w takes row w; afterwards rows come from the
-    // queue in completion order (Sec. 5.5 "Persistent sampled").  Every
-    // workgroup that took a row draws exactly one ticket that ends its loop,
-    // so a launch draws exactly M_live tickets, 0 .. M_live - 1, in the
-    // queue's modification order.  The draw of ticket M_live - 1 is the last
-    // access of the launch to the queue, and that workgroup returns it to
-    // zero; no other ordering is needed.
+    // queue.  The ticket of the next row is drawn when a row starts, so the
+    // next row and its length are known during this row's Phase 1.
     int row = blockIdx.x;
+    uint32_t L = row < m_live ? clamp_len(p.ke[row], p.n) : 0u;
+    bool looked = false;
     while (row < m_live) {
-        select_row<S, DUAL>(p, row, sm, sliceA, sliceB);
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t t = atomicAdd(p.counters, 1u);
-            if (t + 1 == static_cast<uint32_t>(m_live)) atomicExch(p.counters, 0u);
-            sm.next_row = static_cast<int32_t>(G + t);
+        uint32_t t = 0;
+        if (threadIdx.x == 0) t = atomicAdd(p.counters, 1u);
+        NextRow nr = select_row<S, DUAL>(p, row, L, looked, t, m_live, sm, sliceA, sliceB);
+        if (nr.row < 0) {  // routes without a view publish the ticket here
+            if (threadIdx.x == 0) publish_ticket(p, t, m_live, sm);
+            __syncthreads();
+            nr.row = sm.next_row;
+            nr.L = nr.row < m_live ? clamp_len(p.ke[nr.row], p.n) : 0u;
+            nr.looked = false;
         }
         __syncthreads();
-        row = sm.next_row;
+        row = nr.row;
+        L = nr.L;
+        looked = nr.looked;
     }
 }
 
@@ -1217,8 +1392,62 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             h1, h0, k, 0u, outp, k, sm);
         return;
     }
-    // Large frontier: gather the part ranges into one contiguous frontier
-    // (LDS, then region2), count the leading digit, refine through ping-pong
+    // Large frontier.  First the key extremes of the candidates in use, read
+    // range by range with several loads in flight: when every candidate
+    // carries the same key (a constant row, say), no value outside them
+    // ranks above it, so any K of them are the answer and refinement has
+    // nothing to separate; the first K in offset order are taken.
+    {
+        if (threadIdx.x == 0) { sm.kext[0] = kNoElem; sm.kext[1] = 0; }
+        __syncthreads();
+        uint32_t mn = kNoElem, mx = 0;
+        const int kinds = route == TOPKF_ROUTE_BAND ? 2 : 1;
+        for (int kind = 0; kind < kinds; ++kind) {
+            for (uint32_t pp = 0; pp < Pr; ++pp) {
+                const uint32_t c = sm.offs[kind][pp + 1] - sm.offs[kind][pp];
+                const uint32_t s0 = pp * chunk;
+                const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
+                for (uint32_t j0 = 0; j0 < c; j0 += 8 * kBlock) {
+                    uint32_t kk[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t j = j0 + u * kBlock + threadIdx.x;
+                        kk[u] = kNoElem;
+                        if (j < c) kk[u] = nt_load2(region + (kind ? s1 - 1 - j : s0 + j)).y;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t j = j0 + u * kBlock + threadIdx.x;
+                        if (j < c) {
+                            mn = kk[u] < mn ? kk[u] : mn;
+                            mx = kk[u] > mx ? kk[u] : mx;
+                        }
+                    }
+                }
+            }
+        }
+        lds_extremes(&sm.kext[0], mn, mx);
+        __syncthreads();
+        if (sm.kext[0] == sm.kext[1]) {
+            for (uint32_t gi = threadIdx.x; gi < k; gi += kBlock) {
+                const int kind = gi < C0 ? 0 : 1;
+                const uint32_t r = kind ? gi - C0 : gi;
+                const uint32_t* off = sm.offs[kind];
+                uint32_t lo_p = 0, hi_p = Pr;  // the part with off[lo_p] <= r < off[lo_p + 1]
+                while (hi_p - lo_p > 1) {
+                    const uint32_t mid = (lo_p + hi_p) >> 1;
+                    if (off[mid] <= r) lo_p = mid; else hi_p = mid;
+                }
+                const uint32_t j = r - off[lo_p];
+                const uint32_t s0 = lo_p * chunk;
+                const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
+                outp[gi] = static_cast<int32_t>(nt_load2(region + (kind ? s1 - 1 - j : s0 + j)).x);
+            }
+            return;
+        }
+    }
+    // Otherwise gather the part ranges into one contiguous frontier (LDS,
+    // then region2), count the leading digit, refine through ping-pong
     // buffers.
     const Frontier G{sm.front, kFront, region2, &sm.cnt[0]};
     for (uint32_t g0 = 0; g0 < ctot; g0 += 4 * kBlock) {

@@ -196,3 +196,29 @@ def test_spill_rows_constant_and_quantized():
         note("spill rows plan %s" % name)
         out, st, _ = run_topk(x, ke, k, plan=plan)
         assert_exact(out, x, ke, k)
+
+
+def test_tied_candidates_shortcut_boundary():
+    """Rows whose candidates all share one key take the direct tie fill; a
+    single differing value (above, or +0 against -0) must still be separated."""
+    t = topkf()
+    k, n = 2048, 100000
+    rng = np.random.default_rng(11)
+    x = np.empty((6, n), dtype=np.float32)
+    x[0] = 1.0                                   # all candidates tied
+    x[1] = 1.0
+    x[1, rng.integers(0, n)] = 2.0               # one value above the tie
+    x[2] = 1.0
+    x[2, rng.integers(0, n)] = 0.5               # one value below: not a candidate
+    x[3] = -0.0
+    x[3, rng.choice(n, 10, replace=False)] = 0.0  # +0 ranks above -0
+    x[4] = -np.inf
+    x[4, rng.choice(n, 3000, replace=False)] = np.float32(3.4e38)
+    x[5] = np.float32(-1.5)
+    ke = np.array([n, n - 3, n, n - 1000, n, 70001], dtype=np.int32)
+    for name, plan in (("kv-p8", t.make_plan(t.FAMILY_KVSPLIT, 128, 1, splits=8, min_segment=4096)),
+                       ("kv-p3", t.make_plan(t.FAMILY_KVSPLIT, 64, 0, splits=3, min_segment=4096))):
+        note("tied candidate rows plan %s" % name)
+        out, st, _ = run_topk(x, ke, k, plan=plan, stats=True)
+        assert_exact(out, x, ke, k)
+        note("routes %s" % st)
