@@ -155,6 +155,12 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
+// base + the number of set bits of m below this lane.
+__device__ __forceinline__ uint32_t mbcnt_from(uint64_t m, uint32_t base) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), base));
+}
+
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
 }
@@ -557,16 +563,19 @@ __device__ __forceinline__ void load_chunk(const Span& sp, uint32_t base, u32x4 
     }
 }
 
-// Calls f(bits4, index of bits4.x) over every element of the span, with the
-// first chunk (U vectors per thread) and the head/tail elements loaded before
-// pre() runs, so their latency overlaps pre().  Later chunks are double
-// buffered: the next chunk is in flight while the current one is processed.
-// mid() runs exactly once, after the first chunk (or after the head/tail
-// elements when there is no chunk), with the second chunk already in flight.
-// Every thread of the block must call it with the same span.
-template <int U, class Pre, class F, class Mid>
-__device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f, Mid&& mid) {
+// Calls f(bits4, index of bits4.x) over every element of the span.  issue()
+// runs first (loads whose results pre() needs, ahead of the chunk in the
+// in-order load queue), then the first chunk (U vectors per thread) and the
+// head/tail elements are loaded, then pre() runs, so their latency overlaps
+// pre().  Later chunks are double buffered: the next chunk is in flight while
+// the current one is processed.  mid() runs exactly once, after the first
+// chunk (or after the head/tail elements when there is no chunk), with the
+// second chunk already in flight.  Every thread of the block must call it
+// with the same span.
+template <int U, class Issue, class Pre, class F, class Mid>
+__device__ __forceinline__ void scan_span(const Span& sp, Issue&& issue, Pre&& pre, F&& f, Mid&& mid) {
     const uint32_t tid = threadIdx.x;
+    issue();
     u32x4 cur[U];
     if (sp.nvec) load_chunk<U>(sp, 0, cur);
     const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
@@ -593,9 +602,14 @@ struct NoPre {
     __device__ void operator()() const {}
 };
 
+template <int U, class Pre, class F, class Mid>
+__device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f, Mid&& mid) {
+    scan_span<U>(sp, NoPre{}, pre, f, mid);
+}
+
 template <int U, class Pre, class F>
 __device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f) {
-    scan_span<U>(sp, pre, f, NoPre{});
+    scan_span<U>(sp, NoPre{}, pre, f, NoPre{});
 }
 
 // Phase 2 admission of one 4-element group: key <= hi (and key > lo for the
@@ -629,10 +643,25 @@ __device__ __forceinline__ void count_route(const Params& p, int route) {
 // Phase 1: coarse histogram of the view into h (cleared and visible), then
 // tau0/tau1 and their cutoffs into sm.cut[0], sm.cut[1].  All sample loads of
 // a batch are issued before any is used.  Ends with a barrier.
+// The first batch of view samples of phase1 (sample j0 + u * kBlock + tid).
+__device__ __forceinline__ void view_batch(const float* x, uint32_t a, uint32_t nv, int s, uint32_t j0,
+                                           uint32_t (&b)[kSampleVec]) {
+#pragma unroll
+    for (int u = 0; u < kSampleVec; ++u) {
+        const uint32_t j = j0 + u * kBlock + threadIdx.x;
+        b[u] = j < nv ? __float_as_uint(x[a + j * s]) : kNoElem;
+    }
+}
+
 __device__ __forceinline__ void phase1(const float* x, uint32_t a, uint32_t nv, int s, uint32_t q, uint32_t q1,
-                       uint32_t* h, Shared& sm) {
+                       uint32_t* h, Shared& sm, const uint32_t* first = nullptr) {
     const uint32_t tid = threadIdx.x;
-    for (uint32_t j0 = 0; j0 < nv; j0 += kBlock * kSampleVec) {
+    if (first) {
+#pragma unroll
+        for (int u = 0; u < kSampleVec; ++u)
+            if (first[u] != kNoElem) lds_inc(h, coarse_of_bits(first[u]));
+    }
+    for (uint32_t j0 = first ? kBlock * kSampleVec : 0u; j0 < nv; j0 += kBlock * kSampleVec) {
         uint32_t b[kSampleVec];
 #pragma unroll
         for (int u = 0; u < kSampleVec; ++u) {
@@ -1251,25 +1280,52 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     // Phases 1 and 2 for this part; the segment's first chunk is in flight
     // while the (replicated) view is histogrammed.
     uint32_t T0 = 0, T1 = 0;
+    // Candidates are staged in the wave's share of the LDS frontier with
+    // wave-uniform counts (primary from the bottom, band from the top) and
+    // written out once per wave after the scan; a wave whose share fills up
+    // writes the rest straight to its reserved slots.
+    uint2* stg = sm.front + wave() * kWaveCap;
+    uint32_t sp_n = 0, sb_n = 0;
+    uint32_t vb[kSampleVec];
     const Span sp = make_span(x, lo, hi);
     scan_span<kSegVec>(
         sp,
+        [&]() { view_batch(x, g.a, g.nv, S, 0u, vb); },
         [&]() {
             clear_hist(h0);
             if (threadIdx.x == 0) { sm.cnt[0] = 0; sm.cnt[1] = 0; }
             __syncthreads();
-            phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm);
+            phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
             T0 = sm.cut[0];
             T1 = sm.cut[1];
         },
         [&](u32x4 b, uint32_t i0) {
             uint32_t key[4];
             bool pp[4], pb[4];
+            uint64_t mp[4], mb[4];
+            uint32_t tp = 0, tb = 0;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 key[u] = desc_key(b[u]);
                 pp[u] = key[u] <= T0;
                 pb[u] = DUAL && key[u] > T0 && key[u] <= T1;
+                mp[u] = __builtin_amdgcn_ballot_w64(pp[u]);
+                mb[u] = DUAL ? __builtin_amdgcn_ballot_w64(pb[u]) : 0ull;
+                tp += __builtin_popcountll(mp[u]);
+                tb += __builtin_popcountll(mb[u]);
+            }
+            if (sp_n + sb_n + tp + tb <= static_cast<uint32_t>(kWaveCap)) {
+                // Staged in the wave's LDS share: primary upward, band downward.
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (pp[u]) stg[mbcnt_from(mp[u], sp_n)] = make_uint2(i0 + u, key[u]);
+                    sp_n += __builtin_popcountll(mp[u]);
+                    if (DUAL) {
+                        if (pb[u]) stg[kWaveCap - 1 - mbcnt_from(mb[u], sb_n)] = make_uint2(i0 + u, key[u]);
+                        sb_n += __builtin_popcountll(mb[u]);
+                    }
+                }
+                return;
             }
             // kind 0: primary, upward from lo; kind 1: band, downward from hi - 1
             auto emit = [&](const bool (&pr)[4], int kind) {
@@ -1293,7 +1349,30 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             };
             emit(pp, 0);
             if (DUAL) emit(pb, 1);
-        });
+        },
+        NoPre{});
+    // Flush the staged entries: one reservation per wave and kind, then
+    // coalesced stores.  Each wave reads back only its own share.
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    {
+        uint32_t pbase = 0, bbase = 0;
+        if (lane() == 0) {
+            if (sp_n) pbase = atomicAdd(&sm.cnt[0], sp_n);
+            if (DUAL && sb_n) bbase = atomicAdd(&sm.cnt[1], sb_n);
+        }
+        pbase = readlane(pbase, 0);
+        bbase = readlane(bbase, 0);
+        for (uint32_t e = lane(); e < sp_n; e += 64) {
+            const uint2 v = stg[e];
+            nt_store2(region + lo + pbase + e, v.x, v.y);
+        }
+        if (DUAL) {
+            for (uint32_t e = lane(); e < sb_n; e += 64) {
+                const uint2 v = stg[kWaveCap - 1 - e];
+                nt_store2(region + (hi - 1 - (bbase + e)), v.x, v.y);
+            }
+        }
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t* counts = kv_counts(p, row);
