@@ -46,8 +46,6 @@ constexpr int kCapA = 4096;                  // general path: LDS part of Q1 / Q
 constexpr int kRowVec = 4;      // persistent scan: 128-bit loads per thread per chunk
 constexpr int kSegVec = 8;      // KV-split scan: 128-bit loads per thread per chunk
 constexpr int kSampleVec = 8;   // view samples per thread per batch
-constexpr int kLookVec = 2;     // next-row view samples per thread held across a chunk
-constexpr uint32_t kLookMaxView = 65535;  // packed 16-bit lookahead bins
 constexpr int kMaxSplits = 256; // KV-split parts per row
 // A NaN pattern whose descending key is 0xFFFFFFFF: larger than every cutoff,
 // so it marks lanes that hold no element.
@@ -77,7 +75,6 @@ struct Params {
 
 struct alignas(16) Shared {
     uint32_t hist[2][kBins];
-    uint32_t look[kBins / 2];  // persistent: next row's view histogram, two 16-bit bins a word
     uint2 front[kFront];
     uint32_t offs[2][kMaxSplits + 1];  // KV-split finisher: per-part prefix offsets
     alignas(16) uint32_t wsum[3][kWaves];  // per-wave totals: [0] block_find, [1], [2] scans
@@ -432,22 +429,11 @@ __device__ __forceinline__ void clear_hist(uint32_t* h) {
     reinterpret_cast<uint4*>(h)[threadIdx.x] = make_uint4(0, 0, 0, 0);
 }
 
-__device__ __forceinline__ void clear_look(uint32_t* h) {
-    reinterpret_cast<uint2*>(h)[threadIdx.x] = make_uint2(0, 0);
-}
-
-// Adds one to 16-bit bin `bin` of a packed histogram (two bins per word; a
-// bin never exceeds kLookMaxView, so no carry crosses into the neighbour).
-__device__ __forceinline__ void look_inc(uint32_t* h, uint32_t bin) {
-    atomicAdd(h + (bin >> 1), 1u << ((bin & 1u) << 4));
-}
-
 // For each target t[i] (1 <= t[i] <= sum of hist), finds b = min{b : H(b) >=
 // t[i]} and H(b - 1) (Eqs. 15, 23), written to sm.res[2i], sm.res[2i + 1].
 // Each thread owns 4 consecutive bins.  Reads hist before its first barrier
 // and ends with a barrier, so hist may be rewritten right after it returns.
-// PACKED: hist holds two 16-bit bins per word (the lookahead histogram).
-template <int NT, bool PACKED = false>
+template <int NT>
 __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t (&t)[NT], Shared& sm) {
     const uint32_t tid = threadIdx.x;
     // Defaults keep every later LDS index in range should a target exceed
@@ -457,13 +443,7 @@ __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t 
 #pragma unroll
         for (int i = 0; i < NT; ++i) { sm.res[2 * i] = kBins - 1; sm.res[2 * i + 1] = 0; }
     }
-    uint4 v;
-    if (PACKED) {
-        const uint2 w = reinterpret_cast<const uint2*>(hist)[tid];
-        v = make_uint4(w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16);
-    } else {
-        v = reinterpret_cast<const uint4*>(hist)[tid];
-    }
+    const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];
     const uint32_t s = v.x + v.y + v.z + v.w;
     const uint32_t incl = wave_incl_scan(s);
     if (lane() == 63) sm.wsum[0][wave()] = incl;
@@ -568,9 +548,9 @@ __device__ __forceinline__ void load_chunk(const Span& sp, uint32_t base, u32x4 
 // in-order load queue), then the first chunk (U vectors per thread) and the
 // head/tail elements are loaded, then pre() runs, so their latency overlaps
 // pre().  Later chunks are double buffered: the next chunk is in flight while
-// the current one is processed.  mid() runs exactly once, after the first
-// chunk (or after the head/tail elements when there is no chunk), with the
-// second chunk already in flight.  Every thread of the block must call it
+// the current one is processed.  mid() runs exactly once, as the last chunk
+// is taken up (after that chunk's loads were issued), or after the head/tail
+// elements when there is no chunk.  Every thread of the block must call it
 // with the same span.
 template <int U, class Issue, class Pre, class F, class Mid>
 __device__ __forceinline__ void scan_span(const Span& sp, Issue&& issue, Pre&& pre, F&& f, Mid&& mid) {
@@ -587,9 +567,9 @@ __device__ __forceinline__ void scan_span(const Span& sp, Issue&& issue, Pre&& p
         const bool more = base + kBlock * U < sp.nvec;
         u32x4 nxt[U];
         if (more) load_chunk<U>(sp, base + kBlock * U, nxt);
+        else mid();
 #pragma unroll
         for (int u = 0; u < U; ++u) f(cur[u], sp.vlo + 4 * (base + u * kBlock + tid));
-        if (base == 0) mid();
         if (more) {
 #pragma unroll
             for (int u = 0; u < U; ++u) cur[u] = nxt[u];
@@ -984,12 +964,13 @@ __device__ __forceinline__ uint32_t clamp_len(int32_t v, int32_t n) {
     return static_cast<uint32_t>(v < 0 ? 0 : (v > n ? n : v));
 }
 
-// The row a persistent worker takes next, its valid length and whether its
-// view histogram already sits in sm.look (its Phase 1 ran ahead).
+// The row a persistent worker takes next, its valid length and, when its
+// view is usable, the first batch of its view samples (loaded ahead).
 struct NextRow {
     int row;
     uint32_t L;
     bool looked;
+    uint32_t vb[kSampleVec];  // when looked: the row's first batch of view samples
 };
 
 // Ticket of the persistent queue (Sec. 5.5 "Persistent sampled").  A launch
@@ -1006,18 +987,23 @@ __device__ __forceinline__ int publish_ticket(const Params& p, uint32_t t, int m
 }
 
 // One row, whole-row ownership (persistent mapping).  L is the row's valid
-// length; `looked`: sm.look holds the row's view histogram.  Thread 0 holds
-// ticket t, drawn when the row started.  sliceA holds the wave spills, sliceB
-// is the contiguous frontier of the general path.  On the sampled route the
-// next row is published during Phase 1, and that row's view samples are
-// gathered into sm.look while this row's Phase 2 streams (its Phase 1 runs
-// ahead); nr.row < 0 means the next row is not known yet.
+// length; `looked`: vb holds the row's first batch of view samples, loaded
+// at the end of the previous row.  Thread 0 holds ticket t, drawn when the
+// row started.  sliceA holds the wave spills, sliceB is the contiguous
+// frontier of the general path.  On the sampled route the next row is
+// published during Phase 1, its length is read while this row streams, and
+// its first batch of view samples is loaded when this row is done; nr.row <
+// 0 means the next row is not known yet.
 template <int S, bool DUAL>
 __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t L, bool looked,
-                                              uint32_t t, int m_live, Shared& sm, uint2* sliceA,
+                                              const uint32_t (&vb)[kSampleVec], uint32_t t,
+                                              int m_live, Shared& sm, uint2* sliceA,
                                               uint2* sliceB) {
     const uint32_t k = p.k;
-    NextRow nr{-1, 0, false};
+    NextRow nr;
+    nr.row = -1;
+    nr.L = 0;
+    nr.looked = false;
     int32_t* outp = p.out + static_cast<int64_t>(row) * k;
     if (L <= k) {
         sentinel_row(outp, L, k);
@@ -1032,6 +1018,8 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     int route = TOPKF_ROUTE_EXACT_DIRECT;
     bool certified = false;
     uint32_t C = 0;
+    uint32_t na = 0, nnv = 0;  // the next row's view
+    const float* xn = nullptr;
     if constexpr (S > 0) {
         uint32_t a;
         const uint32_t nv = view_size<S>(row, L, &a);
@@ -1039,10 +1027,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
         if (nv >= q1) {
             uint32_t T0 = 0, T1 = 0;
             int32_t ke_next = 0;
-            uint32_t na = 0, nnv = 0;
-            const float* xn = nullptr;
             bool on = false;
-            uint32_t nb[kLookVec];
             const Span sp = make_span(x, 0, L);
             scan_span<kRowVec>(
                 sp,
@@ -1052,21 +1037,9 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                         sm.out_cnt = 0;
                         publish_ticket(p, t, m_live, sm);
                     }
-                    if (looked) {
-                        const uint32_t tg[2] = {q, q1};
-                        block_find<2, true>(sm.look, tg, sm);
-                        clear_look(sm.look);
-                        if (wave() < 2) {
-                            const uint32_t c = wave_cutoff(sm.res[2 * wave()]);
-                            if (lane() == 0) sm.cut[wave()] = c;
-                        }
-                        __syncthreads();
-                    } else {
-                        clear_hist(h0);
-                        clear_look(sm.look);
-                        __syncthreads();
-                        phase1(x, a, nv, S, q, q1, h0, sm);
-                    }
+                    clear_hist(h0);
+                    __syncthreads();
+                    phase1(x, a, nv, S, q, q1, h0, sm, looked ? vb : nullptr);
                     T0 = sm.cut[0];
                     T1 = sm.cut[1];
                     nr.row = sm.next_row;
@@ -1074,36 +1047,14 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                 },
                 [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, wf, h1); },
                 [&]() {
-                    // The next row's geometry and first sample batch, in flight
-                    // while the rest of this row streams.
+                    // The next row's geometry (its length has arrived by now).
                     nr.L = nr.row < m_live ? clamp_len(ke_next, p.n) : 0u;
                     if (nr.L > k) {
                         nnv = view_size<S>(static_cast<uint32_t>(nr.row), nr.L, &na);
-                        on = nnv >= q1 && nnv <= kLookMaxView;
+                        on = nnv >= q1;
                         xn = p.logits + static_cast<int64_t>(nr.row) * p.stride;
                     }
-#pragma unroll
-                    for (int u = 0; u < kLookVec; ++u) {
-                        const uint32_t j = u * kBlock + threadIdx.x;
-                        nb[u] = on && j < nnv ? __float_as_uint(xn[na + j * S]) : kNoElem;
-                    }
                 });
-            if (on) {
-#pragma unroll
-                for (int u = 0; u < kLookVec; ++u)
-                    if (nb[u] != kNoElem) look_inc(sm.look, coarse_of_bits(nb[u]));
-                for (uint32_t j0 = kBlock * kLookVec; j0 < nnv; j0 += kBlock * kSampleVec) {
-                    uint32_t b[kSampleVec];
-#pragma unroll
-                    for (int u = 0; u < kSampleVec; ++u) {
-                        const uint32_t j = j0 + u * kBlock + threadIdx.x;
-                        b[u] = j < nnv ? __float_as_uint(xn[na + j * S]) : kNoElem;
-                    }
-#pragma unroll
-                    for (int u = 0; u < kSampleVec; ++u)
-                        if (b[u] != kNoElem) look_inc(sm.look, coarse_of_bits(b[u]));
-                }
-            }
             nr.looked = on;
             C = publish_waves(wf, sm);
             route = TOPKF_ROUTE_PRIMARY;
@@ -1134,6 +1085,12 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     for (int w = 0; w < kWaves; ++w) spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
     if (spill) count_route(p, TOPKF_ROUTE_SPILL);
     finish_waves(C, sliceA, wsl, sliceB, sliceA, h1, h0, kq, outp, k, sm);
+    // The next row's first batch of view samples goes out now, so that its
+    // Phase 1 overlaps the loads of its first chunk and the sampled lines are
+    // still cached when its scan reads them.
+    if constexpr (S > 0) {
+        if (nr.looked) view_batch(xn, na, nnv, S, 0u, nr.vb);
+    }
     return nr;
 }
 
@@ -1149,10 +1106,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     int row = blockIdx.x;
     uint32_t L = row < m_live ? clamp_len(p.ke[row], p.n) : 0u;
     bool looked = false;
+    uint32_t vb[kSampleVec];
+#pragma unroll
+    for (int u = 0; u < kSampleVec; ++u) vb[u] = kNoElem;
     while (row < m_live) {
         uint32_t t = 0;
         if (threadIdx.x == 0) t = atomicAdd(p.counters, 1u);
-        NextRow nr = select_row<S, DUAL>(p, row, L, looked, t, m_live, sm, sliceA, sliceB);
+        NextRow nr = select_row<S, DUAL>(p, row, L, looked, vb, t, m_live, sm, sliceA, sliceB);
         if (nr.row < 0) {  // routes without a view publish the ticket here
             if (threadIdx.x == 0) publish_ticket(p, t, m_live, sm);
             __syncthreads();
@@ -1164,6 +1124,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         row = nr.row;
         L = nr.L;
         looked = nr.looked;
+#pragma unroll
+        for (int u = 0; u < kSampleVec; ++u) vb[u] = nr.vb[u];
     }
 }
 
