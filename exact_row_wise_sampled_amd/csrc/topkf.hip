@@ -86,7 +86,7 @@ struct alignas(16) Shared {
     uint32_t cut[2];
     int32_t next_row;
     uint32_t flag;
-    uint32_t kext[2];  // KV-split finisher: smallest and largest candidate key
+    uint32_t kext[2];  // smallest and largest key of a large frontier
 };
 static_assert(sizeof(Shared) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
@@ -889,17 +889,21 @@ __device__ __forceinline__ void refine(Frontier cur, Frontier nxt, uint32_t* hc,
     }
 }
 
-// Copies every wave's frontier entries (LDS share, then its spill) into
-// dst[0, C) in wave order.  Ends with a barrier.
-__device__ __forceinline__ void compact_waves(const uint2* spill_base, int64_t spill_len,
+// Copies the wave frontiers (LDS share, then spill range) into one
+// contiguous frontier dst and returns whether all of its keys are equal
+// (block-uniform; ends with a barrier).
+__device__ __forceinline__ bool compact_waves(const uint2* spill_base, int64_t spill_len,
                                               uint2* dst, Shared& sm) {
     if (threadIdx.x == 0) {
         uint32_t o = 0;
         for (int w = 0; w < kWaves; ++w) { sm.offs[0][w] = o; o += sm.wcnt[w]; }
         sm.offs[0][kWaves] = o;
+        sm.kext[0] = kNoElem;
+        sm.kext[1] = 0;
     }
     __syncthreads();
     const uint32_t C = sm.offs[0][kWaves];
+    uint32_t mn = kNoElem, mx = 0;
     for (uint32_t g = threadIdx.x; g < C; g += kBlock) {
         uint32_t w = 0;
         while (w + 1 < kWaves && sm.offs[0][w + 1] <= g) ++w;
@@ -912,8 +916,12 @@ __device__ __forceinline__ void compact_waves(const uint2* spill_base, int64_t s
             v = make_uint2(t.x, t.y);
         }
         nt_store2(dst + g, v.x, v.y);
+        mn = v.y < mn ? v.y : mn;
+        mx = v.y > mx ? v.y : mx;
     }
+    lds_extremes(&sm.kext[0], mn, mx);
     __syncthreads();
+    return sm.kext[0] == sm.kext[1];
 }
 
 // Phase 3 for a wave-private frontier of C entries (sizes in sm.wcnt, visible),
@@ -945,7 +953,13 @@ __device__ __forceinline__ void finish_waves(uint32_t C, const uint2* spill_base
             h1, h0, kq, out_base, outp, k, sm);
         return;
     }
-    compact_waves(spill_base, spill_len, contig, sm);
+    if (compact_waves(spill_base, spill_len, contig, sm)) {
+        // Every entry carries the same key (a constant row, say): no value
+        // outside the frontier ranks above it, so its first kq entries are
+        // the rest of the answer.
+        for (uint32_t j = threadIdx.x; j < kq; j += kBlock) outp[out_base + j] = static_cast<int32_t>(contig[j].x);
+        return;
+    }
     if (threadIdx.x == 0) sm.cnt[0] = C;
     __syncthreads();
     const Frontier cur{sm.front, 0, contig, &sm.cnt[0]};
