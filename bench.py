@@ -72,21 +72,24 @@ def measured_traffic(config: str):
 
 
 def stream_read_reference(dev, nbytes: int = 1 << 30) -> float:
-    """GB/s of a plain library reduction that reads nbytes once (context for the
-    fraction of achievable bandwidth)."""
+    """GB/s of the library's plain 128-bit streaming-read kernel over nbytes
+    (topkf_read_probe, the same loads the selector streams with): the
+    achievable-bandwidth reference for the selector's score-row GB/s."""
     import torch
+    from exact_row_wise_sampled_amd import topkf
     x = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
-    for _ in range(2):
-        x.sum()
+    for _ in range(3):
+        topkf.read_probe(x, sink)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(5):
-        x.sum()
+    for _ in range(10):
+        topkf.read_probe(x, sink)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 5
+    ms = e0.elapsed_time(e1) / 10
     del x
     return nbytes / (ms * 1e-3) / 1e9
 

@@ -72,6 +72,8 @@ _lib.topkf_plan_workspace_size.argtypes = [_c.POINTER(Plan), _i64, _i64, _c.POIN
                                            _c.POINTER(_sz)]
 _lib.topkf_coarse_keys.restype = _i32
 _lib.topkf_coarse_keys.argtypes = [_vp, _i64, _vp, _vp]
+_lib.topkf_read_probe.restype = _i32
+_lib.topkf_read_probe.argtypes = [_vp, _i64, _vp, _vp]
 
 
 class TopkfError(RuntimeError):
@@ -175,6 +177,14 @@ def coarse_keys(x, out, stream=None) -> None:
         raise ValueError("size mismatch")
     st = _stream_handle(stream, x.device)
     _check(_lib.topkf_coarse_keys(x.data_ptr(), x.numel(), out.data_ptr(), st), "topkf_coarse_keys")
+
+
+def read_probe(x, sink, stream=None) -> None:
+    """Plain 128-bit streaming read of the whole tensor x (the bandwidth
+    reference); sink is a one-element int32/uint32 device tensor."""
+    st = _stream_handle(stream, x.device)
+    _check(_lib.topkf_read_probe(x.data_ptr(), x.numel() * x.element_size(), sink.data_ptr(), st),
+           "topkf_read_probe")
 
 
 class Selector:

@@ -180,6 +180,18 @@ topkf_status topk_filtered_debug(const float* logits, int64_t num_rows, int64_t 
  */
 topkf_status topkf_coarse_keys(const float* x, int64_t n, uint16_t* out, hipStream_t stream);
 
+/*
+ * Measurement aid, not part of the pages' API: a plain streaming read of
+ * `bytes` bytes at x with the same 128-bit nontemporal loads the selector
+ * streams with (two 512-thread workgroups per compute unit, four loads in
+ * flight per thread), so that its rate is the achievable-bandwidth reference
+ * for the selector's score-row GB/s.  x: device pointer, 16-byte aligned;
+ * bytes: a multiple of 16, >= 0; sink: device pointer to one uint32 that the
+ * kernel writes only in an improbable case (keeps the loads live).  Returns
+ * TOPKF_EINVAL for a misaligned pointer or size, TOPKF_EHIP on launch failure.
+ */
+topkf_status topkf_read_probe(const void* x, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -161,3 +161,22 @@ def test_coarse_keys_match_ieee_fp16():
     bad = np.flatnonzero(got != want)
     assert bad.size == 0, "first mismatch x=%r got %d want %d" % (x[bad[0]], got[bad[0]], want[bad[0]])
     assert want[x == np.inf].tolist() == [31] * int((x == np.inf).sum())
+
+
+def test_read_probe():
+    """The streaming-read reference: validates alignment and size, reads a
+    buffer without writing its sink for ordinary data."""
+    import torch
+    from exact_row_wise_sampled_amd import topkf
+    from tests.gpu_util import dev
+    d = dev()
+    x = torch.ones(1 << 20, dtype=torch.float32, device=d)
+    sink = torch.zeros(1, dtype=torch.int32, device=d)
+    topkf.read_probe(x, sink)
+    topkf.read_probe(x[:4], sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    with pytest.raises(topkf.TopkfError):
+        topkf.read_probe(x[1:5], sink)   # 4-byte offset: not 16-byte aligned
+    with pytest.raises(topkf.TopkfError):
+        topkf.read_probe(x[:3], sink)    # 12 bytes: not a multiple of 16
