@@ -674,10 +674,12 @@ __device__ __forceinline__ uint32_t publish_waves(const WaveFrontier& wf, Shared
 }
 
 // Exact coarse route (Sec. 4.3, Eq. 20) over [0, L): coarse histogram of
-// every value, tau* = min{b : C(b) >= K}, then one classification pass that
+// every value, tau* = min{b : C(b) >= K}, then one classification pass (from
+// registers when the row fits one chunk, else a second read) that
 // commits c < tau* to the output and retains c == tau* in the wave frontier
 // with its leading-digit histogram in h0.  Returns k0 = K - |E0|; the
 // committed count is left in sm.out_cnt and the frontier sizes in sm.wcnt.
+template <bool REGS>
 __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint32_t k,
                                                 int32_t* outp, WaveFrontier& wf, uint32_t* hc,
                                                 uint32_t* h0, Shared& sm) {
@@ -688,16 +690,13 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
     wf.n = 0;
     __syncthreads();
     const Span sp = make_span(x, 0, L);
-    scan_span<kRowVec>(sp, NoPre{}, [&](u32x4 b, uint32_t) {
+    auto count = [&](u32x4 b, uint32_t) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             if (b[u] != kNoElem) lds_inc(hc, coarse_of_bits(b[u]));
-    });
-    __syncthreads();
-    const uint32_t t[1] = {k};
-    block_find<1>(hc, t, sm);
-    const uint32_t tau = sm.res[0], before = sm.res[1];
-    scan_span<kRowVec>(sp, NoPre{}, [&](u32x4 b, uint32_t i0) {
+    };
+    uint32_t tau = 0;
+    auto classify = [&](u32x4 b, uint32_t i0) {
         bool com[4], ret[4];
         uint32_t idx[4], key[4], bin[4];
 #pragma unroll
@@ -712,7 +711,37 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
         }
         commit4(com, idx, outp, k, sm);
         wappend4(ret, idx, key, bin, wf, h0);
-    });
+    };
+    const uint32_t t[1] = {k};
+    if (REGS && sp.nvec <= static_cast<uint32_t>(kBlock * kRowVec)) {
+        // A row of at most one chunk stays in registers: one read serves the
+        // histogram and the classification (Sec. 5.5 "Row-local exact").
+        const uint32_t tid = threadIdx.x;
+        u32x4 v[kRowVec];
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u) v[u] = u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
+        if (sp.nvec) load_chunk<kRowVec>(sp, 0, v);
+        const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
+        const u32x4 sb{tid < sp.nscal ? __float_as_uint(sp.x[se]) : kNoElem, kNoElem, kNoElem, kNoElem};
+        count(sb, se);
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u) count(v[u], 0u);
+        __syncthreads();
+        block_find<1>(hc, t, sm);
+        tau = sm.res[0];
+        const uint32_t before = sm.res[1];
+        if (sp.nscal) classify(sb, se);
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u) classify(v[u], sp.vlo + 4 * (u * kBlock + tid));
+        publish_waves(wf, sm);
+        return k - before;
+    }
+    scan_span<kRowVec>(sp, NoPre{}, count);
+    __syncthreads();
+    block_find<1>(hc, t, sm);
+    tau = sm.res[0];
+    const uint32_t before = sm.res[1];
+    scan_span<kRowVec>(sp, NoPre{}, classify);
     publish_waves(wf, sm);
     return k - before;
 }
@@ -1088,7 +1117,8 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     }
     uint32_t kq = k;
     if (!certified) {
-        kq = exact_route(x, L, k, outp, wf, h0, h1, sm);
+        // The no-view plan serves short rows: keep them in registers.
+        kq = exact_route<S == 0>(x, L, k, outp, wf, h0, h1, sm);
         C = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) C += sm.wcnt[w];
@@ -1208,7 +1238,7 @@ __device__ __forceinline__ void kv_exact_row(const Params& p, const RowGeom& g, 
     uint2* region2 = region + slice_len(p.n);
     const int64_t wsl = wave_spill_len(p.n);
     WaveFrontier wf{sm.front + wave() * kWaveCap, region + wave() * wsl, 0};
-    const uint32_t kq = exact_route(x, g.L, k, outp, wf, sm.hist[0], sm.hist[1], sm);
+    const uint32_t kq = exact_route<true>(x, g.L, k, outp, wf, sm.hist[0], sm.hist[1], sm);
     uint32_t C = 0;
     bool spill = false;
 #pragma unroll
