@@ -44,7 +44,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape",
 class Plan(ctypes.Structure):
     _fields_ = [("family", ctypes.c_int32), ("stride", ctypes.c_int32), ("dual", ctypes.c_int32),
                 ("splits", ctypes.c_int32), ("workers", ctypes.c_int32),
-                ("min_segment", ctypes.c_int32), ("band_quarters", ctypes.c_int32)]
+                ("min_segment", ctypes.c_int32), ("band_quarters", ctypes.c_int32),
+                ("primary_quarters", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -106,8 +107,9 @@ def plan_for(num_rows: int, max_kv_len: int, cu_count: int) -> Plan:
 
 
 def make_plan(family: int, stride: int, dual: int = 1, splits: int = 1, workers: int = 1,
-              min_segment: int = 8192, band_quarters: int = 7) -> Plan:
-    return Plan(family, stride, dual, splits, workers, min_segment, band_quarters)
+              min_segment: int = 8192, band_quarters: int = 7,
+              primary_quarters: int = 6) -> Plan:
+    return Plan(family, stride, dual, splits, workers, min_segment, band_quarters, primary_quarters)
 
 
 def plan_workspace_size(plan: Plan, num_rows: int, max_kv_len: int) -> tuple[int, int]:

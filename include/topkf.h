@@ -129,8 +129,11 @@ typedef struct {
     int32_t min_segment; /* KV-split: shortest segment in elements; a row of
                             length L uses min(P, ceil(L / min_segment)) parts */
     int32_t band_quarters; /* secondary target K~1 = ceil(band_quarters * K / 4),
-                              7..32 when dual (paper Sec. 6.4 uses 1.75K, i.e. 7);
-                              ignored without dual */
+                              above primary_quarters and at most 32 when dual
+                              (paper Sec. 6.4 uses 1.75K, i.e. 7); ignored
+                              without dual */
+    int32_t primary_quarters; /* primary target K~ = ceil(primary_quarters * K / 4),
+                                 4..31 (paper Sec. 4.2 uses 1.5K, i.e. 6) */
 } topkf_plan;
 
 /*

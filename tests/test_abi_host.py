@@ -96,6 +96,9 @@ def test_workspace_sizes_follow_the_plan():
     for bad in (topkf.make_plan(7, 128), topkf.make_plan(1, 32), topkf.make_plan(1, 64, dual=2),
                 topkf.make_plan(1, 64, workers=0), topkf.make_plan(2, 64, splits=0),
                 topkf.make_plan(2, 64, splits=257),
-                topkf.make_plan(2, 64, splits=2, min_segment=0)):
+                topkf.make_plan(2, 64, splits=2, min_segment=0),
+                topkf.make_plan(1, 64, 1, workers=2, band_quarters=6),
+                topkf.make_plan(1, 64, 0, workers=2, primary_quarters=3),
+                topkf.make_plan(1, 128, 1, workers=2, primary_quarters=7, band_quarters=7)):
         with pytest.raises(topkf.TopkfError):
             topkf.plan_workspace_size(bad, 5, n)
