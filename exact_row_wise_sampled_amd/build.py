@@ -15,6 +15,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep the compiler from forming packed FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # room for the compile-time table of FP32 cutoffs per coarse bin
+    "-fconstexpr-steps=100000000",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -118,6 +118,71 @@ __device__ __forceinline__ uint32_t coarse_of_bits(uint32_t b) {
     return k16 >> 5;
 }
 
+// The inclusive FP32 cutoff of every coarse bin, computed at compile time
+// (Sec. 4.3: the largest non-NaN descending key whose value still has
+// c <= tau; c is monotone in the key, so {c(x) <= tau} == {key(x) <= T(tau)}).
+// fp16_rne_bits is IEEE round-to-nearest-even FP32 -> FP16 in integer
+// arithmetic (overflow to infinity from 65520 up, FP16 subnormals kept), the
+// conversion coarse_of_bits gets from the hardware; a test compares the whole
+// table with the device's own search over coarse_of_bits.  T(tau) is
+// kKeyFirst - 1 (admits no non-NaN value) when even +inf lies above tau.
+constexpr uint32_t fp16_rne_bits(uint32_t f) {
+    const uint32_t s = (f >> 16) & 0x8000u;
+    const uint32_t a = f & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return s | 0x7E00u;   // NaN
+    if (a >= 0x477FF000u) return s | 0x7C00u;  // 65520 and up round to infinity
+    if (a >= 0x38800000u) {                    // FP16 normal range, from 2^-14
+        uint32_t v = (a >> 13) - (112u << 10);  // rebias the exponent, keep 10 mantissa bits
+        const uint32_t rem = a & 0x1FFFu;
+        if (rem > 0x1000u || (rem == 0x1000u && (v & 1u))) v += 1;
+        return s | v;
+    }
+    const uint32_t e = a >> 23;
+    if (e < 102) return s;                     // below 2^-25: zero
+    const uint32_t m = (a & 0x7FFFFFu) | 0x800000u;
+    const uint32_t sh = 126 - e;               // value / 2^-24 = m >> sh
+    uint32_t v = m >> sh;
+    const uint32_t rem = m & ((1u << sh) - 1u);
+    const uint32_t half = 1u << (sh - 1u);
+    if (rem > half || (rem == half && (v & 1u))) v += 1;
+    return s | v;
+}
+
+constexpr uint32_t coarse_of_key_exact(uint32_t k) {
+    const uint32_t b = k ^ ((~static_cast<uint32_t>(static_cast<int32_t>(k) >> 31)) >> 1);
+    const uint32_t h = fp16_rne_bits(b);
+    const uint32_t k16 = (h & 0x8000u) ? h : (h ^ 0x7FFFu);
+    return k16 >> 5;
+}
+
+struct CutTable {
+    uint32_t v[kBins];
+};
+
+constexpr CutTable make_cut_table() {
+    CutTable t{};
+    for (uint32_t tau = 0; tau < static_cast<uint32_t>(kBins); ++tau) {
+        if (coarse_of_key_exact(kKeyFirst) > tau) {
+            t.v[tau] = kKeyFirst - 1;
+            continue;
+        }
+        if (coarse_of_key_exact(kKeyLast) <= tau) {
+            t.v[tau] = kKeyLast;
+            continue;
+        }
+        uint32_t lo = kKeyFirst, hi = kKeyLast;  // c(lo) <= tau < c(hi)
+        while (hi - lo > 1) {
+            const uint32_t mid = lo + (hi - lo) / 2;
+            if (coarse_of_key_exact(mid) <= tau) lo = mid;
+            else hi = mid;
+        }
+        t.v[tau] = lo;
+    }
+    return t;
+}
+
+__constant__ CutTable kCutoff = make_cut_table();
+
 // Refinement digit j of a descending key: 11 + 11 + 10 bits, most
 // significant first (Sec. 4.3 "D = 3 digits of widths 11 + 11 + 10").
 __device__ __forceinline__ uint32_t digit(int j, uint32_t key) {
@@ -162,6 +227,11 @@ __device__ __forceinline__ uint32_t mbcnt_from(uint64_t m, uint32_t base) {
 
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+
+// A value every lane holds alike, moved to a scalar register.
+__device__ __forceinline__ uint32_t readfirst(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
@@ -482,7 +552,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total,
 }
 
 // Sec. 4.3: the inclusive FP32 cutoff of coarse bin tau, as the largest
-// non-NaN descending key whose value still has c <= tau.  c is monotone in the
+// non-NaN descending key whose value still has c <= tau, searched on the
+// device with the hardware conversion (the check of the compile-time table).  c is monotone in the
 // key, so {c(x) <= tau} == {key(x) <= cutoff(tau)}.  A 64-way search by one
 // whole wave: each round splits the interval over the lanes.  Returns
 // kKeyFirst - 1 (admits no non-NaN value) when even +inf lies above tau.
@@ -622,9 +693,6 @@ __device__ __forceinline__ void count_route(const Params& p, int route) {
     if (p.stats && threadIdx.x == 0) atomicAdd(p.stats + route, 1u);
 }
 
-// Phase 1: coarse histogram of the view into h (cleared and visible), then
-// tau0/tau1 and their cutoffs into sm.cut[0], sm.cut[1].  All sample loads of
-// a batch are issued before any is used.  Ends with a barrier.
 // The first batch of view samples of phase1 (sample j0 + u * kBlock + tid).
 __device__ __forceinline__ void view_batch(const float* x, uint32_t a, uint32_t nv, int s, uint32_t j0,
                                            uint32_t (&b)[kSampleVec]) {
@@ -635,7 +703,17 @@ __device__ __forceinline__ void view_batch(const float* x, uint32_t a, uint32_t 
     }
 }
 
-__device__ __forceinline__ void phase1(const float* x, uint32_t a, uint32_t nv, int s, uint32_t q, uint32_t q1,
+// The FP32 cutoffs T(tau0) and T(tau1) of Phase 1 (block-uniform).
+struct Cuts {
+    uint32_t t0, t1;
+};
+
+// Phase 1: coarse histogram of the view into h (cleared and visible; `first`
+// is the first batch of samples when it was loaded ahead), tau0 and tau1
+// (Eq. 15), and their inclusive FP32 cutoffs from the compile-time table.
+// All sample loads of a batch are issued before any is used.  Ends with a
+// barrier.
+__device__ __forceinline__ Cuts phase1(const float* x, uint32_t a, uint32_t nv, int s, uint32_t q, uint32_t q1,
                        uint32_t* h, Shared& sm, const uint32_t* first = nullptr) {
     const uint32_t tid = threadIdx.x;
     if (first) {
@@ -657,12 +735,8 @@ __device__ __forceinline__ void phase1(const float* x, uint32_t a, uint32_t nv, 
     __syncthreads();
     const uint32_t t[2] = {q, q1};
     block_find<2>(h, t, sm);
-    const uint32_t tau0 = sm.res[0], tau1 = sm.res[2];
-    if (wave() < 2) {
-        const uint32_t c = wave_cutoff(wave() == 0 ? tau0 : tau1);
-        if (lane() == 0) sm.cut[wave()] = c;
-    }
-    __syncthreads();
+    const uint32_t tau0 = readfirst(sm.res[0]), tau1 = readfirst(sm.res[2]);
+    return Cuts{kCutoff.v[tau0], kCutoff.v[tau1]};
 }
 
 // Records each wave's frontier size and returns the total (ends with a barrier).
@@ -1036,7 +1110,7 @@ __device__ __forceinline__ int publish_ticket(const Params& p, uint32_t t, int m
 // at the end of the previous row.  Thread 0 holds ticket t, drawn when the
 // row started.  sliceA holds the wave spills, sliceB is the contiguous
 // frontier of the general path.  On the sampled route the next row is
-// published during Phase 1, its length is read while this row streams, and
+// published at the end of Phase 1, its length is read while this row streams, and
 // its first batch of view samples is loaded when this row is done; nr.row <
 // 0 means the next row is not known yet.
 template <int S, bool DUAL>
@@ -1078,15 +1152,16 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                 sp,
                 [&]() {
                     clear_hist(h1);
-                    if (threadIdx.x == 0) {
-                        sm.out_cnt = 0;
-                        publish_ticket(p, t, m_live, sm);
-                    }
                     clear_hist(h0);
+                    if (threadIdx.x == 0) sm.out_cnt = 0;
                     __syncthreads();
-                    phase1(x, a, nv, S, q, q1, h0, sm, looked ? vb : nullptr);
-                    T0 = sm.cut[0];
-                    T1 = sm.cut[1];
+                    const Cuts c = phase1(x, a, nv, S, q, q1, h0, sm, looked ? vb : nullptr);
+                    T0 = c.t0;
+                    T1 = c.t1;
+                    // The next row, drawn when this row started, is published
+                    // now: the draw's latency hid behind Phase 1.
+                    if (threadIdx.x == 0) publish_ticket(p, t, m_live, sm);
+                    __syncthreads();
                     nr.row = sm.next_row;
                     if (nr.row < m_live) ke_next = p.ke[nr.row];
                 },
@@ -1303,9 +1378,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             clear_hist(h0);
             if (threadIdx.x == 0) { sm.cnt[0] = 0; sm.cnt[1] = 0; }
             __syncthreads();
-            phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
-            T0 = sm.cut[0];
-            T1 = sm.cut[1];
+            const Cuts c = phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
+            T0 = c.t0;
+            T1 = c.t1;
         },
         [&](u32x4 b, uint32_t i0) {
             uint32_t key[4];
@@ -1598,6 +1673,17 @@ __global__ __launch_bounds__(kBlock) void read_probe_kernel(const u32x4* x, int6
     if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// One wave per coarse bin: the compile-time cutoff and the device search.
+__global__ __launch_bounds__(kBlock) void cutoff_check_kernel(uint32_t* table, uint32_t* search) {
+    const uint32_t tau = blockIdx.x * kWaves + wave();
+    if (tau >= static_cast<uint32_t>(kBins)) return;
+    const uint32_t c = wave_cutoff(tau);
+    if (lane() == 0) {
+        table[tau] = kCutoff.v[tau];
+        search[tau] = c;
+    }
+}
+
 __global__ void coarse_keys_kernel(const float* x, int64_t n, uint16_t* out) {
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -1850,6 +1936,12 @@ topkf_status topkf_read_probe(const void* x, int64_t bytes, uint32_t* sink, hipS
     if (blocks > need) blocks = need;
     hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
                        static_cast<const u32x4*>(x), nvec, sink);
+    return hipGetLastError() == hipSuccess ? TOPKF_OK : TOPKF_EHIP;
+}
+
+topkf_status topkf_coarse_cutoffs(uint32_t* table, uint32_t* search, hipStream_t stream) {
+    if (!table || !search) return TOPKF_EINVAL;
+    hipLaunchKernelGGL(cutoff_check_kernel, dim3(kBins / kWaves), dim3(kBlock), 0, stream, table, search);
     return hipGetLastError() == hipSuccess ? TOPKF_OK : TOPKF_EHIP;
 }
 

@@ -73,6 +73,8 @@ _lib.topkf_plan_workspace_size.argtypes = [_c.POINTER(Plan), _i64, _i64, _c.POIN
                                            _c.POINTER(_sz)]
 _lib.topkf_coarse_keys.restype = _i32
 _lib.topkf_coarse_keys.argtypes = [_vp, _i64, _vp, _vp]
+_lib.topkf_coarse_cutoffs.restype = _i32
+_lib.topkf_coarse_cutoffs.argtypes = [_vp, _vp, _vp]
 _lib.topkf_read_probe.restype = _i32
 _lib.topkf_read_probe.argtypes = [_vp, _i64, _vp, _vp]
 
@@ -179,6 +181,15 @@ def coarse_keys(x, out, stream=None) -> None:
         raise ValueError("size mismatch")
     st = _stream_handle(stream, x.device)
     _check(_lib.topkf_coarse_keys(x.data_ptr(), x.numel(), out.data_ptr(), st), "topkf_coarse_keys")
+
+
+def coarse_cutoffs(table, search, stream=None) -> None:
+    """table, search: 2048-element int32/uint32 device tensors; see
+    topkf_coarse_cutoffs in include/topkf.h."""
+    if table.numel() < 2048 or search.numel() < 2048:
+        raise ValueError("need 2048 entries")
+    st = _stream_handle(stream, table.device)
+    _check(_lib.topkf_coarse_cutoffs(table.data_ptr(), search.data_ptr(), st), "topkf_coarse_cutoffs")
 
 
 def read_probe(x, sink, stream=None) -> None:

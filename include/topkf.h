@@ -184,6 +184,17 @@ topkf_status topk_filtered_debug(const float* logits, int64_t num_rows, int64_t 
 topkf_status topkf_coarse_keys(const float* x, int64_t n, uint16_t* out, hipStream_t stream);
 
 /*
+ * The inclusive FP32 cutoff T(tau) of every coarse bin (paper Sec. 4.3: the
+ * largest non-NaN descending key whose value has c <= tau; kKeyFirst - 1 =
+ * 0x007FFFFE when even +inf lies above tau).  The selector reads these from a
+ * table computed at compile time; this call writes that table to table[0,
+ * 2048) and the device's own search over the hardware conversion to
+ * search[0, 2048), so that tests can check one against the other.
+ * table, search: device pointers to 2048 uint32 each.  TOPKF_EINVAL on null.
+ */
+topkf_status topkf_coarse_cutoffs(uint32_t* table, uint32_t* search, hipStream_t stream);
+
+/*
  * Measurement aid, not part of the pages' API: a plain streaming read of
  * `bytes` bytes at x with the same 128-bit nontemporal loads the selector
  * streams with (two 512-thread workgroups per compute unit, four loads in

@@ -31,7 +31,7 @@ def test_header_declares_the_api():
     names = declared_functions()
     for want in ("topk_filtered_workspace_size", "topk_filtered", "topkf_status_string",
                  "topkf_plan_for", "topkf_plan_workspace_size", "topk_filtered_debug",
-                 "topkf_coarse_keys", "topkf_read_probe"):
+                 "topkf_coarse_keys", "topkf_read_probe", "topkf_coarse_cutoffs"):
         assert want in names, names
 
 

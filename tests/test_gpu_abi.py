@@ -180,3 +180,37 @@ def test_read_probe():
         topkf.read_probe(x[1:5], sink)   # 4-byte offset: not 16-byte aligned
     with pytest.raises(topkf.TopkfError):
         topkf.read_probe(x[:3], sink)    # 12 bytes: not a multiple of 16
+
+
+def test_cutoff_table_matches_search_and_ieee():
+    """The compile-time cutoff table T(tau) equals the device's search over
+    the hardware FP16 conversion for every coarse bin, and numpy's IEEE FP16
+    conversion confirms it is the last key of bin <= tau (paper Sec. 4.3)."""
+    import torch
+    from exact_row_wise_sampled_amd import topkf
+    from tests.gpu_util import dev
+    d = dev()
+    table = torch.zeros(2048, dtype=torch.int32, device=d)
+    search = torch.zeros(2048, dtype=torch.int32, device=d)
+    topkf.coarse_cutoffs(table, search)
+    torch.cuda.synchronize()
+    tab = table.cpu().numpy().view(np.uint32)
+    sea = search.cpu().numpy().view(np.uint32)
+    assert np.array_equal(tab, sea), np.nonzero(tab != sea)[0][:10]
+
+    def coarse_of_keys(k):
+        k = k.astype(np.uint32)
+        b = np.where(k & np.uint32(0x80000000), k, k ^ np.uint32(0x7FFFFFFF)).astype(np.uint32)
+        with np.errstate(over="ignore"):
+            h = b.view(np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
+        return np.where(h & 0x8000, h, h ^ 0x7FFF) >> 5
+
+    tau = np.arange(2048, dtype=np.uint32)
+    none = tab == 0x007FFFFE          # even +inf lies above tau
+    full = tab == 0xFF800000          # every non-NaN value is admitted
+    assert np.all(coarse_of_keys(np.array([0x007FFFFF]))[0] > tau[none])
+    mid = ~none & ~full
+    assert np.all(coarse_of_keys(tab[mid]) <= tau[mid])
+    assert np.all(coarse_of_keys(tab[mid] + 1) > tau[mid])
+    assert np.all(coarse_of_keys(tab[full]) <= tau[full])
+    assert np.all(np.diff(tab.astype(np.int64)) >= 0)   # monotone in tau
