@@ -25,6 +25,10 @@ if not os.path.exists(LIB_PATH):
     raise ImportError("topkf HIP library not built: %s is missing "
                       "(run exact_row_wise_sampled_amd.build.build())" % LIB_PATH)
 
+# torch first: the library then binds to the HIP runtime torch has loaded, so
+# both share one runtime instance whatever the caller imported first.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 K_MAX = 2048
