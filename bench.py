@@ -104,13 +104,13 @@ def cpu_baseline(w, seconds: float) -> dict:
         oracle.topk(w.x, w.ke, w.k, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 50:
+        if el >= seconds or reps >= 10000:
             break
     per_call = el / reps
     return {"value": round(w.score_bytes() / per_call / 1e9, 4), "unit": "GB/s",
             "rows_per_s": round(w.m / per_call, 1), "cores": threads, "kind": "oracle",
-            "sample": "whole %s batch (%d rows) x %d repetitions, %.1f s wall" % (
-                w.name, w.m, reps, el)}
+            "sample": "whole %s batch (%d rows) x %d repetitions, %.1f s wall on %d threads "
+                      "(%.0f thread-seconds)" % (w.name, w.m, reps, el, threads, el * threads)}
 
 
 def main() -> int:
@@ -119,7 +119,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", default="decode", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--eager", action="store_true",
