@@ -63,3 +63,24 @@ def assert_exact(out: np.ndarray, x: np.ndarray, ke: np.ndarray, k: int, m_live=
     # rows at or beyond M_live are untouched
     if res.rows < m:
         assert (out[res.rows:] == canary).all(), "rows >= M_live were written"
+
+
+def assert_routes(st: dict, x: np.ndarray, ke: np.ndarray, k: int, plan, m_live=None) -> dict:
+    """The selector's route counters equal the CPU route model's counts for
+    every exclusive route (the spill counter is an extra, capacity-dependent
+    tally and is not modelled).  `plan` is the plan the call ran with."""
+    from oracle import route_model as rm
+    pol = rm.Policy(int(plan.stride), bool(plan.dual), int(plan.primary_quarters),
+                    int(plan.band_quarters))
+    want = rm.route_counts(x, ke, k, pol, m_live=m_live)
+    got = {name: int(st[name]) for name in rm.ROUTES}
+    assert got == want, "routes: selector %s, model %s" % (got, want)
+    return want
+
+
+def auto_plan(m: int, n: int):
+    """The plan the library picks on this device for an (M_cap, N) call."""
+    import torch
+    from exact_row_wise_sampled_amd import topkf
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return topkf.plan_for(m, n, cus)

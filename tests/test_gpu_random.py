@@ -5,12 +5,13 @@ automatic one or a forced family / view / band / primary / split / worker
 setting), runs the selector through the C ABI and checks the oracle's exact
 criterion (value multiset bit-identical, every index strictly above the K-th
 value selected, distinct in-range indices, sentinel layout, rows >= M_live
-untouched).  Sizes keep the oracle to seconds.
+untouched), and that the route counters equal the CPU route model's counts.
+Sizes keep the oracle to seconds.
 """
 import numpy as np
 import pytest
 
-from tests.gpu_util import assert_exact, note, run_topk
+from tests.gpu_util import assert_exact, assert_routes, auto_plan, note, run_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -88,5 +89,6 @@ def test_random_case(case):
     m_live = int(rng.integers(0, m + 1)) if rng.random() < 0.2 else None
     plan, pname = _plan(rng, t)
     note("random case %d: M=%d N=%d K=%d %s live=%s plan %s" % (case, m, n, k, kind, m_live, pname))
-    out, _, _ = run_topk(x, ke, k, m_live=m_live, plan=plan)
+    out, st, _ = run_topk(x, ke, k, m_live=m_live, plan=plan, stats=True)
     assert_exact(out, x, ke, k, m_live=m_live)
+    assert_routes(st, x, ke, k, plan if plan is not None else auto_plan(m, n), m_live=m_live)
