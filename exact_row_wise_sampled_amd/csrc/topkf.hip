@@ -1741,12 +1741,14 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
     if (occupancy < 1) occupancy = 1;
     topkf_plan r{};
     // View policy (Sec. 5.5: s = 64 and s = 128 compile-time policies;
-    // Sec. 6.4: sampling pays off for wide rows, exact localization for short).
-    if (n < 16384) r.stride = 0;
-    else if (n < 65536) r.stride = 64;
-    else r.stride = 128;
+    // Sec. 6.4 Fig. 12: sampling pays off for wide rows, exact localization
+    // for short ones).  Measured on MI355X at K = 2048 over M = 64..4096:
+    // the exact route wins below 8K columns, the two are even at 8K, the
+    // view wins from 12K on, and s = 128 is as fast as or faster than s = 64
+    // from 12K up (up to 12 % at 128K), so s = 64 is left to explicit plans.
+    r.stride = n < 12288 ? 0 : 128;
     r.dual = r.stride ? 1 : 0;
-    r.min_segment = 8192;
+    r.min_segment = 16384;
     // Secondary target K~1 = 2.5K (Sec. 4.6 treats K~ and K~1 as efficiency
     // knobs).  With the pages' 1.75K some causal-prefill rows (about 2 per
     // 1000) underfill both boundaries and recover through a whole-row exact
@@ -1755,9 +1757,25 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
     r.band_quarters = 10;
     r.primary_quarters = 6;
     const int64_t pool = static_cast<int64_t>(cus) * occupancy;
-    if (r.stride == 0 || m_cap >= pool) {
+    const int64_t rows = m_cap > 0 ? m_cap : 1;
+    // Mapping (Sec. 5.5).  With at least a full pool of rows, persistent
+    // workers.  With a quarter of the pool or fewer, one workgroup per row
+    // unless the rows are long: KV-split pays for its second launch and its
+    // replicated views only from N >= 2048 * max(M, 64) columns (measured:
+    // M = 64 gains 9 % at N = 128K, M = 128 breaks even at 256K, and every
+    // M up to 64 loses at 64K).  In between, KV-split: one workgroup per row
+    // is about 20 % faster on i.i.d. rows but a row whose admitted tail is
+    // most of the row (constant or heavily tied) then streams its whole
+    // frontier through one workgroup, 3-4 times slower on the adversarial
+    // mix, where the split spreads it over the parts.
+    bool kv = false;
+    if (r.stride != 0 && m_cap < pool) {
+        if (4 * rows > pool) kv = true;
+        else kv = n >= 2048 * (rows > 64 ? rows : 64);
+    }
+    if (!kv) {
         r.family = TOPKF_FAMILY_PERSISTENT;
-        r.workers = static_cast<int32_t>(m_cap < pool ? (m_cap > 0 ? m_cap : 1) : pool);
+        r.workers = static_cast<int32_t>(m_cap < pool ? rows : pool);
         r.splits = 1;
         // A worker that recovers an underfilled row holds up the end of the
         // launch; on causal prefill K~ = 1.75K underfills about 0.3 % of rows
@@ -1766,8 +1784,11 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         // KV-split keeps 1.5K: its parts collect the band in the same pass.
         r.primary_quarters = 7;
     } else {
+        // Parts per row: enough to fill the pool, but no segment shorter
+        // than 16K columns (shorter segments lose more to the replicated
+        // view than they gain in span).
         r.family = TOPKF_FAMILY_KVSPLIT;
-        int64_t P = (pool + m_cap - 1) / (m_cap > 0 ? m_cap : 1);
+        int64_t P = (pool + rows - 1) / rows;
         int64_t pmax = (n + r.min_segment - 1) / r.min_segment;
         if (pmax > kMaxSplits) pmax = kMaxSplits;
         if (P > pmax) P = pmax;

@@ -66,7 +66,19 @@ def test_planner_maps_workload_shapes():
     assert long_.family == topkf.FAMILY_KVSPLIT
     assert long_.splits <= 524288 // long_.min_segment
     mid = topkf.plan_for(1024, 32768, cus)
-    assert mid.stride == 64
+    assert mid.stride == 128 and mid.family == topkf.FAMILY_PERSISTENT
+    assert topkf.plan_for(1024, 12288, cus).stride == 128
+    assert topkf.plan_for(1024, 8192, cus).stride == 0
+    # Few rows: one workgroup per row unless the rows are long.
+    for m, n, fam in ((64, 65536, topkf.FAMILY_PERSISTENT), (4, 65536, topkf.FAMILY_PERSISTENT),
+                      (4, 131072, topkf.FAMILY_KVSPLIT), (128, 131072, topkf.FAMILY_PERSISTENT),
+                      (128, 262144, topkf.FAMILY_KVSPLIT), (256, 65536, topkf.FAMILY_KVSPLIT),
+                      (256, 262144, topkf.FAMILY_KVSPLIT), (512, 262144, topkf.FAMILY_PERSISTENT)):
+        pl = topkf.plan_for(m, n, cus)
+        assert pl.family == fam, (m, n, pl)
+        if fam == topkf.FAMILY_PERSISTENT:
+            assert pl.workers == min(m, 2 * cus)
+    assert long_.splits == 32 and decode.splits == 8
 
 
 def test_planner_is_deterministic_and_validates():
