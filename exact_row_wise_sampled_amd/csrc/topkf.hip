@@ -86,7 +86,7 @@ struct alignas(16) Shared {
     uint32_t tie_cnt;
     uint32_t cut[2];
     int32_t next_row;
-    uint32_t flag;
+    uint32_t part_max;  // KV-split finisher: the largest candidate count of one part
     uint32_t kext[2];  // smallest and largest key of a large frontier
 };
 static_assert(sizeof(Shared) <= 80 * 1024, "two workgroups per CU must fit in LDS");
@@ -1490,11 +1490,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         cp = counts[2 * threadIdx.x];
         cb = counts[2 * threadIdx.x + 1];
     }
+    if (threadIdx.x == 0) sm.part_max = 0;
     clear_hist(h1);
     uint32_t C0 = 0, CB = 0;
     const uint32_t op = block_excl_scan(cp, &C0, sm, 1);
     const uint32_t ob = block_excl_scan(cb, &CB, sm, 2);
     if (threadIdx.x < Pr) { sm.offs[0][threadIdx.x] = op; sm.offs[1][threadIdx.x] = ob; }
+    {
+        const uint32_t mx = wave_max(cp > cb ? cp : cb);
+        if (lane() == 0 && mx) __hip_atomic_fetch_max(&sm.part_max, mx, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if (threadIdx.x == 0) {
         sm.offs[0][Pr] = C0;
         sm.offs[1][Pr] = CB;
@@ -1513,39 +1519,60 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     count_route(p, route);
     __syncthreads();  // offsets visible
     if (ctot <= static_cast<uint32_t>(kBlock * kRegs)) {
-        // Each thread locates its candidates (the part p with off[p] <= r <
-        // off[p + 1]) with a branch-free binary search, all kRegs at once, and
-        // loads them straight into registers.
+        // Register slots: when no part holds more than cap = 2^lc candidates
+        // of a kind, with nr * cap <= kBlock * kRegs for the nr part ranges in
+        // use, range q takes slots [q cap, (q + 1) cap) and a slot finds its
+        // candidate by a shift and a mask.  Otherwise each slot locates its
+        // candidate (the part p with off[p] <= r < off[p + 1]) with a
+        // branch-free binary search over the LDS offsets.
+        const uint32_t nr = route == TOPKF_ROUTE_BAND ? 2 * Pr : Pr;
+        uint32_t lc = 13;
+        while (lc > 0 && (nr << lc) > static_cast<uint32_t>(kBlock * kRegs)) --lc;
         uint32_t src[kRegs];
-        uint32_t pstep = 1;
-        while (pstep * 2 <= Pr) pstep *= 2;
+        bool live[kRegs];
+        if (sm.part_max <= (1u << lc)) {
 #pragma unroll
-        for (int u = 0; u < kRegs; ++u) src[u] = 0;
-        for (uint32_t step = pstep; step > 0; step >>= 1) {
+            for (int u = 0; u < kRegs; ++u) {
+                const uint32_t gq = threadIdx.x + kBlock * u;
+                const uint32_t q = gq >> lc, j = gq & ((1u << lc) - 1u);
+                const uint32_t kind = q >= Pr ? 1u : 0u;
+                const uint32_t pp = q < nr ? q - kind * Pr : 0u;
+                live[u] = q < nr && j < sm.offs[kind][pp + 1] - sm.offs[kind][pp];
+                const uint32_t s0 = pp * chunk;
+                const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
+                src[u] = kind ? s1 - 1 - j : s0 + j;
+            }
+        } else {
+            uint32_t pstep = 1;
+            while (pstep * 2 <= Pr) pstep *= 2;
+#pragma unroll
+            for (int u = 0; u < kRegs; ++u) src[u] = 0;
+            for (uint32_t step = pstep; step > 0; step >>= 1) {
+#pragma unroll
+                for (int u = 0; u < kRegs; ++u) {
+                    const uint32_t gi = threadIdx.x + kBlock * u;
+                    const int kind = gi < C0 ? 0 : 1;
+                    const uint32_t r = kind ? gi - C0 : gi;
+                    const uint32_t cand = src[u] + step;
+                    if (gi < ctot && cand < Pr && sm.offs[kind][cand] <= r) src[u] = cand;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < kRegs; ++u) {
                 const uint32_t gi = threadIdx.x + kBlock * u;
                 const int kind = gi < C0 ? 0 : 1;
                 const uint32_t r = kind ? gi - C0 : gi;
-                const uint32_t cand = src[u] + step;
-                if (gi < ctot && cand < Pr && sm.offs[kind][cand] <= r) src[u] = cand;
+                const uint32_t pp = src[u];
+                const uint32_t j = gi < ctot ? r - sm.offs[kind][pp] : 0;
+                const uint32_t s0 = pp * chunk;
+                const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
+                src[u] = kind ? s1 - 1 - j : s0 + j;
+                live[u] = gi < ctot;
             }
-        }
-#pragma unroll
-        for (int u = 0; u < kRegs; ++u) {
-            const uint32_t gi = threadIdx.x + kBlock * u;
-            const int kind = gi < C0 ? 0 : 1;
-            const uint32_t r = kind ? gi - C0 : gi;
-            const uint32_t pp = src[u];
-            const uint32_t j = gi < ctot ? r - sm.offs[kind][pp] : 0;
-            const uint32_t s0 = pp * chunk;
-            const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
-            src[u] = kind ? s1 - 1 - j : s0 + j;
         }
         refine_regs<kRegs, true>(
             [&](int u, uint32_t& i, uint32_t& key) {
-                const uint32_t gi = threadIdx.x + kBlock * u;
-                if (gi >= ctot) return false;
+                if (!live[u]) return false;
                 const u32x2 t2 = nt_load2(region + src[u]);
                 i = t2.x;
                 key = t2.y;

@@ -222,3 +222,31 @@ def test_tied_candidates_shortcut_boundary():
         out, st, _ = run_topk(x, ke, k, plan=plan, stats=True)
         assert_exact(out, x, ke, k)
         note("routes %s" % st)
+
+
+def test_kv_finisher_slot_layouts():
+    """The KV-split finisher maps each part's candidates to fixed register
+    slots when no part holds more than its share, and searches the part
+    offsets otherwise.  Rows whose tail sits in one segment (ascending,
+    descending, a block of large values in the middle) force the search;
+    i.i.d. rows take the direct map; both with and without the band."""
+    t = topkf()
+    k, n = 2048, 65536
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((8, n), dtype=np.float32)
+    x[0] = np.sort(x[0])                          # tail in the last segment
+    x[1] = np.sort(x[1])[::-1]                    # tail in the first segment
+    x[2, 30000:34000] += np.float32(6.0)          # tail inside one middle segment
+    x[3, ::8] += np.float32(4.0)                  # tail spread evenly
+    ke = np.array([n, n, n, n, n - 5, 40000, 20000, n], dtype=np.int32)
+    plans = (("kv-p8-primary", t.make_plan(t.FAMILY_KVSPLIT, 128, 0, splits=8, min_segment=4096,
+                                           primary_quarters=8)),
+             ("kv-p8-dual", t.make_plan(t.FAMILY_KVSPLIT, 128, 1, splits=8, min_segment=4096,
+                                        band_quarters=10, primary_quarters=6)),
+             ("kv-p16-tight", t.make_plan(t.FAMILY_KVSPLIT, 64, 1, splits=16, min_segment=2048,
+                                          band_quarters=6, primary_quarters=4)))
+    for name, plan in plans:
+        note("kv finisher slot layouts plan %s" % name)
+        out, st, _ = run_topk(x, ke, k, plan=plan, stats=True)
+        assert_exact(out, x, ke, k)
+        note("routes %s" % st)
