@@ -1425,7 +1425,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 for (int u = 0; u < 4; ++u) {
                     if (pr[u]) {
                         const uint32_t slot = base + mbcnt(m[u]);
-                        nt_store2(region + (kind ? hi - 1 - slot : lo + slot), i0 + u, key[u]);
+                        region[kind ? hi - 1 - slot : lo + slot] = make_uint2(i0 + u, key[u]);
                     }
                     base += __builtin_popcountll(m[u]);
                 }
@@ -1435,7 +1435,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         },
         NoPre{});
     // Flush the staged entries: one reservation per wave and kind, then
-    // coalesced stores.  Each wave reads back only its own share.
+    // coalesced stores.  Each wave reads back only its own share.  Plain
+    // (cached) stores: the row's finisher runs on the same XCD and reads
+    // them back from its L2 (nontemporal stores cost it 0.5 us on decode).
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     {
         uint32_t pbase = 0, bbase = 0;
@@ -1447,12 +1449,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         bbase = readlane(bbase, 0);
         for (uint32_t e = lane(); e < sp_n; e += 64) {
             const uint2 v = stg[e];
-            nt_store2(region + lo + pbase + e, v.x, v.y);
+            region[lo + pbase + e] = v;
         }
         if (DUAL) {
             for (uint32_t e = lane(); e < sb_n; e += 64) {
                 const uint2 v = stg[kWaveCap - 1 - e];
-                nt_store2(region + (hi - 1 - (bbase + e)), v.x, v.y);
+                region[hi - 1 - (bbase + e)] = v;
             }
         }
     }
@@ -1573,7 +1575,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         refine_regs<kRegs, true>(
             [&](int u, uint32_t& i, uint32_t& key) {
                 if (!live[u]) return false;
-                const u32x2 t2 = nt_load2(region + src[u]);
+                const uint2 t2 = region[src[u]];
                 i = t2.x;
                 key = t2.y;
                 return true;
