@@ -88,6 +88,7 @@ struct alignas(16) Shared {
     int32_t next_row;
     uint32_t part_max;  // KV-split finisher: the largest candidate count of one part
     uint32_t kext[2];  // smallest and largest key of a large frontier
+    uint32_t small_n;  // register refinement: entries in the small boundary list
 };
 static_assert(sizeof(Shared) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
@@ -850,6 +851,7 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
         for (int u = 0; u < R; ++u)
             if ((act >> u) & 1u) lds_inc(hc, key[u] >> 21);
     }
+    if (threadIdx.x == 0) sm.small_n = 0;
     __syncthreads();  // entries are in registers; the frontier buffer becomes the stage
     uint32_t* stage = reinterpret_cast<uint32_t*>(sm.front);
     const uint32_t base0 = out_base;
@@ -895,6 +897,35 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
             }
         }
         if (last) break;
+        if (inb <= 64) {
+            // A boundary group of at most 64 entries is finished by one wave:
+            // gathered into a list (in hn, free from here on), each entry's
+            // rank among the group by full key (equal keys by list position)
+            // is its order, and the `need` first take the remaining slots.
+            // The same selection the remaining digit rounds would make.
+            uint2* list = reinterpret_cast<uint2*>(hn);
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                const bool kp = (keep >> u) & 1u;
+                const uint64_t m = __ballot(kp);
+                if (m) {
+                    const uint32_t base = wave_reserve(&sm.small_n, m, __builtin_popcountll(m));
+                    if (kp) list[base + mbcnt(m)] = make_uint2(idx[u], key[u]);
+                }
+            }
+            __syncthreads();
+            if (wave() == 0) {
+                const uint32_t l = lane();
+                const uint2 mine = l < inb ? list[l] : make_uint2(0u, kNoElem);
+                uint32_t rank = 0;
+                for (uint32_t e = 0; e < inb; ++e) {
+                    const uint32_t ke = readlane(mine.y, static_cast<int>(e));
+                    rank += (ke < mine.y || (ke == mine.y && e < l)) ? 1u : 0u;
+                }
+                if (l < inb && rank < need) stage[out_base + tot_c + rank] = mine.x;
+            }
+            break;
+        }
 #pragma unroll
         for (int u = 0; u < R; ++u)
             if ((keep >> u) & 1u) lds_inc(hn, digit(j + 1, key[u]));

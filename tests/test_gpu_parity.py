@@ -250,3 +250,26 @@ def test_kv_finisher_slot_layouts():
         out, st, _ = run_topk(x, ke, k, plan=plan, stats=True)
         assert_exact(out, x, ke, k)
         note("routes %s" % st)
+
+
+def test_small_boundary_group_with_ties():
+    """When the boundary digit group shrinks to at most 64 entries, one wave
+    orders it by full key; copies of the K-th value straddling the boundary
+    must be split exactly (some selected, the rest not)."""
+    t = topkf()
+    k, n = 2048, 70000
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((6, n), dtype=np.float32)
+    for r, copies in enumerate((3, 9, 40, 63, 64, 200)):
+        v = np.sort(x[r])[::-1][k - 1]              # the K-th value
+        pos = rng.choice(n, copies, replace=False)
+        x[r, pos] = v                                # ties across the boundary
+    ke = np.full(6, n, dtype=np.int32)
+    for name, plan in (("persistent", t.make_plan(t.FAMILY_PERSISTENT, 128, 1, workers=6,
+                                                  band_quarters=10, primary_quarters=7)),
+                       ("kv-p4", t.make_plan(t.FAMILY_KVSPLIT, 128, 0, splits=4,
+                                             min_segment=4096, primary_quarters=8)),
+                       ("exact", t.make_plan(t.FAMILY_PERSISTENT, 0, 0, workers=3))):
+        note("small boundary group plan %s" % name)
+        out, _, _ = run_topk(x, ke, k, plan=plan)
+        assert_exact(out, x, ke, k)
