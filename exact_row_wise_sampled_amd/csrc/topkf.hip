@@ -847,9 +847,34 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
         if (load(u, idx[u], key[u])) act |= 1u << u;
     }
     if (BUILD_H0) {
+        // The leading digits of a candidate tail crowd into a few bins next
+        // to the cutoff's, where 64 lanes adding to one LDS word serialize.
+        // Entries in the wave's four highest leading-digit bins (the values
+        // nearest the cutoff) are counted in registers and added once per
+        // wave; the rest (the spread-out larger values) count themselves.
+        uint32_t dmax = 0;
 #pragma unroll
         for (int u = 0; u < R; ++u)
-            if ((act >> u) & 1u) lds_inc(hc, key[u] >> 21);
+            if ((act >> u) & 1u) dmax = (key[u] >> 21) > dmax ? (key[u] >> 21) : dmax;
+        dmax = wave_max(dmax);
+        uint32_t c[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            if ((act >> u) & 1u) {
+                const uint32_t off = dmax - (key[u] >> 21);
+                if (off < 4) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) c[i] += off == static_cast<uint32_t>(i) ? 1u : 0u;
+                } else {
+                    lds_inc(hc, key[u] >> 21);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t tot = readlane(wave_incl_scan(c[i]), 63);
+            if (lane() == 0 && tot && dmax >= static_cast<uint32_t>(i)) lds_add(hc, dmax - i, tot);
+        }
     }
     if (threadIdx.x == 0) sm.small_n = 0;
     __syncthreads();  // entries are in registers; the frontier buffer becomes the stage
