@@ -1281,7 +1281,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     // queue.  The ticket of the next row is drawn when a row starts, so the
     // next row and its length are known during this row's Phase 1.
     int row = blockIdx.x;
-    uint32_t L = row < m_live ? clamp_len(p.ke[row], p.n) : 0u;
+    // The first row's length is loaded alongside the live-row count.
+    const int32_t ke0 = row < p.m_cap ? p.ke[row] : 0;
+    uint32_t L = row < m_live ? clamp_len(ke0, p.n) : 0u;
     bool looked = false;
     uint32_t vb[kSampleVec];
 #pragma unroll
@@ -1331,12 +1333,12 @@ struct RowGeom {
     bool usable;
 };
 
-// Everything both KV-split kernels derive from (row, ke) alone.
+// Everything both KV-split kernels derive from (row, ke[row]) alone.
 template <int S, bool DUAL>
-__device__ __forceinline__ RowGeom kv_geom(const Params& p, uint32_t row) {
+__device__ __forceinline__ RowGeom kv_geom(const Params& p, uint32_t row, int32_t ke_row) {
     RowGeom g{};
     g.row = row;
-    g.L = clamp_len(p.ke[row], p.n);
+    g.L = clamp_len(ke_row, p.n);
     g.usable = false;
     if constexpr (S > 0) {
         g.nv = view_size<S>(row, g.L, &g.a);
@@ -1392,10 +1394,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     const uint32_t li = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     const uint32_t row = li / P, part = li % P;
     if (row >= static_cast<uint32_t>(p.m_cap)) return;
-    const uint32_t m_live = clamp_len(*p.num_valid_rows, p.m_cap);
+    // Both loads in flight at once (ke has M_cap entries).
+    const int32_t nvr = *p.num_valid_rows;
+    const int32_t ke_row = p.ke[row];
+    const uint32_t m_live = clamp_len(nvr, p.m_cap);
     if (row >= m_live) return;
     const uint32_t k = p.k;
-    const RowGeom g = kv_geom<S, DUAL>(p, row);
+    const RowGeom g = kv_geom<S, DUAL>(p, row, ke_row);
     if (g.L <= k) {
         if (part == 0) {
             sentinel_row(p.out + static_cast<int64_t>(row) * k, g.L, k);
@@ -1529,25 +1534,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     const uint32_t per_xcd = gridDim.x / 8;
     const uint32_t row = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (row >= static_cast<uint32_t>(p.m_cap)) return;
-    const uint32_t m_live = clamp_len(*p.num_valid_rows, p.m_cap);
+    // The live-row count, the row's length and the parts' counts are loaded
+    // together; counts of parts the row did not use this call are stale and
+    // are dropped below.
+    const int32_t nvr = *p.num_valid_rows;
+    const int32_t ke_row = p.ke[row];
+    const uint32_t* counts = kv_counts(p, row);
+    uint32_t cp = 0, cb = 0;
+    if (threadIdx.x < static_cast<uint32_t>(p.splits)) {
+        cp = counts[2 * threadIdx.x];
+        cb = counts[2 * threadIdx.x + 1];
+    }
+    const uint32_t m_live = clamp_len(nvr, p.m_cap);
     if (row >= m_live) return;
     const uint32_t k = p.k;
-    const RowGeom g = kv_geom<S, DUAL>(p, row);
+    const RowGeom g = kv_geom<S, DUAL>(p, row, ke_row);
     if (g.L <= k || !g.usable) return;  // finished by the scan kernel
     const uint32_t L = g.L, Pr = g.Pr, chunk = g.chunk;
     int32_t* outp = p.out + static_cast<int64_t>(row) * k;
     uint2* region = kv_region(p, row);
     uint2* region2 = region + slice_len(p.n);
-    const uint32_t* counts = kv_counts(p, row);
     uint32_t* h0 = sm.hist[0];
     uint32_t* h1 = sm.hist[1];
 
     // Merge the parts (Eq. 27): prefix offsets of the primary and band counts.
-    uint32_t cp = 0, cb = 0;
-    if (threadIdx.x < Pr) {
-        cp = counts[2 * threadIdx.x];
-        cb = counts[2 * threadIdx.x + 1];
-    }
+    if (threadIdx.x >= Pr) { cp = 0; cb = 0; }
     if (threadIdx.x == 0) sm.part_max = 0;
     clear_hist(h1);
     uint32_t C0 = 0, CB = 0;
