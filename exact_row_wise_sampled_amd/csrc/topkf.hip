@@ -47,6 +47,10 @@ constexpr int kRowVec = 4;      // persistent scan: 128-bit loads per thread per
 constexpr int kSegVec = 8;      // KV-split scan: 128-bit loads per thread per chunk
 constexpr int kSampleVec = 8;   // view samples per thread per batch
 constexpr int kMaxSplits = 256; // KV-split parts per row
+// Counter buffer: kCounterHead u32 slots ([0] the persistent queue), two
+// slot counters per row (cooperative exact route), then for KV-split plans
+// without a view one 2048-bin coarse histogram per row.
+constexpr int kCounterHead = 64;
 // A NaN pattern whose descending key is 0xFFFFFFFF: larger than every cutoff,
 // so it marks lanes that hold no element.
 constexpr uint32_t kNoElem = 0xFFFFFFFFu;
@@ -1749,6 +1753,256 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     refine(G, nxt, h1, h0, k, outp, k, sm);
 }
 
+// Cooperative exact coarse route (Sec. 5.5 "Eight-CTA exact cluster": with
+// only a few long rows and no view, the row's segments go to several
+// workgroups; without distributed shared memory their histograms merge in
+// global memory).  Four kernels on the stream, the kernel boundaries making
+// each step's global writes visible to the next:
+//   kvx_hist_kernel      each part counts the coarse keys c(x) of its segment
+//                        and adds its histogram into the row's histogram in
+//                        the counter buffer;
+//   kvx_cut_kernel       one workgroup per row reads (and clears) that
+//                        histogram and finds tau* = min{b : C(b) >= K} and
+//                        |E0| = C(tau* - 1) (Eq. 20);
+//   kvx_classify_kernel  each part rescans its segment, committing c < tau*
+//                        straight to the output and appending c == tau* to
+//                        the row's frontier, through the row's two slot
+//                        counters (staged per wave in LDS, one reservation per
+//                        flush);
+//   kvx_finish_kernel    one workgroup per row refines the frontier for the
+//                        remaining K - |E0| slots and zeroes the row's counters.
+// The commit predicate is the same device c(x) in both passes, so exactly
+// |E0| indices are committed.
+
+__device__ __forceinline__ uint32_t* kvx_hist(const Params& p, uint32_t row) {
+    return p.counters + kCounterHead + 2 * static_cast<int64_t>(p.m_cap) +
+           static_cast<int64_t>(row) * kBins;
+}
+
+__device__ __forceinline__ uint32_t* kvx_ctr(const Params& p, uint32_t row) {
+    return p.counters + kCounterHead + 2 * static_cast<int64_t>(row);
+}
+
+// The (row, part) of a part workgroup (same numbering as the KV-split scan,
+// the parts of a row on one XCD) and of a per-row workgroup.
+__device__ __forceinline__ void kvx_part(const Params& p, uint32_t* row, uint32_t* part) {
+    const uint32_t P = static_cast<uint32_t>(p.splits);
+    const uint32_t per_xcd = gridDim.x / 8;
+    const uint32_t li = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    *row = li / P;
+    *part = li % P;
+}
+
+__device__ __forceinline__ uint32_t kvx_row(void) {
+    const uint32_t per_xcd = gridDim.x / 8;
+    return (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvx_hist_kernel(Params p) {
+    __shared__ Shared sm;
+    uint32_t row, part;
+    kvx_part(p, &row, &part);
+    if (row >= static_cast<uint32_t>(p.m_cap)) return;
+    const int32_t nvr = *p.num_valid_rows;
+    const int32_t ke_row = p.ke[row];
+    if (row >= clamp_len(nvr, p.m_cap)) return;
+    const uint32_t k = p.k;
+    const RowGeom g = kv_geom<0, false>(p, row, ke_row);
+    if (g.L <= k) {
+        if (part == 0) {
+            sentinel_row(p.out + static_cast<int64_t>(row) * k, g.L, k);
+            count_route(p, TOPKF_ROUTE_SENTINEL);
+        }
+        return;
+    }
+    if (part >= g.Pr) return;
+    const uint32_t lo = part * g.chunk < g.L ? part * g.chunk : g.L;
+    const uint32_t hi = lo + g.chunk < g.L ? lo + g.chunk : g.L;
+    uint32_t* h = sm.hist[0];
+    clear_hist(h);
+    __syncthreads();
+    const Span sp = make_span(p.logits + static_cast<int64_t>(row) * p.stride, lo, hi);
+    scan_span<kSegVec>(sp, NoPre{}, [&](u32x4 b, uint32_t) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool v = b[u] != kNoElem;
+            const uint64_t m = __ballot(v);
+            if (m) hist_add(h, v ? coarse_of_bits(b[u]) : 0u, v, m);
+        }
+    });
+    __syncthreads();
+    uint32_t* gh = kvx_hist(p, row);
+    const uint4 c = reinterpret_cast<const uint4*>(h)[threadIdx.x];
+    const uint32_t b0 = 4 * threadIdx.x;
+    if (c.x) atomicAdd(gh + b0, c.x);
+    if (c.y) atomicAdd(gh + b0 + 1, c.y);
+    if (c.z) atomicAdd(gh + b0 + 2, c.z);
+    if (c.w) atomicAdd(gh + b0 + 3, c.w);
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvx_cut_kernel(Params p) {
+    __shared__ Shared sm;
+    const uint32_t row = kvx_row();
+    if (row >= static_cast<uint32_t>(p.m_cap)) return;
+    const int32_t nvr = *p.num_valid_rows;
+    const int32_t ke_row = p.ke[row];
+    if (row >= clamp_len(nvr, p.m_cap)) return;
+    if (clamp_len(ke_row, p.n) <= static_cast<uint32_t>(p.k)) return;
+    // Read the merged histogram and return it to zero (this is its only reader).
+    uint32_t* gh = kvx_hist(p, row);
+    uint32_t* h = sm.hist[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t b = 4 * threadIdx.x + i;
+        h[b] = gh[b];
+        gh[b] = 0;
+    }
+    __syncthreads();
+    const uint32_t t[1] = {static_cast<uint32_t>(p.k)};
+    block_find<1>(h, t, sm);
+    if (threadIdx.x == 0) {
+        uint32_t* rec = kv_counts(p, row);
+        rec[0] = sm.res[0];  // tau*
+        rec[1] = sm.res[1];  // |E0| = C(tau* - 1)
+    }
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvx_classify_kernel(Params p) {
+    __shared__ Shared sm;
+    uint32_t row, part;
+    kvx_part(p, &row, &part);
+    if (row >= static_cast<uint32_t>(p.m_cap)) return;
+    const int32_t nvr = *p.num_valid_rows;
+    const int32_t ke_row = p.ke[row];
+    if (row >= clamp_len(nvr, p.m_cap)) return;
+    const uint32_t k = p.k;
+    const RowGeom g = kv_geom<0, false>(p, row, ke_row);
+    if (g.L <= k || part >= g.Pr) return;
+    const uint32_t tau = kv_counts(p, row)[0];
+    const uint32_t lo = part * g.chunk < g.L ? part * g.chunk : g.L;
+    const uint32_t hi = lo + g.chunk < g.L ? lo + g.chunk : g.L;
+    int32_t* outp = p.out + static_cast<int64_t>(row) * k;
+    uint2* region = kv_region(p, row);
+    uint32_t* ctr = kvx_ctr(p, row);  // [0] committed slots, [1] frontier entries
+    // Wave-private stage: commits from the bottom, frontier entries from the top.
+    uint2* stg = sm.front + wave() * kWaveCap;
+    uint32_t sc_n = 0, sq_n = 0;
+    auto flush = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        uint32_t cb = 0, qb = 0;
+        if (lane() == 0) {
+            if (sc_n) cb = atomicAdd(&ctr[0], sc_n);
+            if (sq_n) qb = atomicAdd(&ctr[1], sq_n);
+        }
+        cb = readlane(cb, 0);
+        qb = readlane(qb, 0);
+        for (uint32_t e = lane(); e < sc_n; e += 64) {
+            const uint32_t slot = cb + e;
+            if (slot < k) outp[slot] = static_cast<int32_t>(stg[e].x);
+        }
+        for (uint32_t e = lane(); e < sq_n; e += 64) region[qb + e] = stg[kWaveCap - 1 - e];
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        sc_n = 0;
+        sq_n = 0;
+    };
+    const Span sp = make_span(p.logits + static_cast<int64_t>(row) * p.stride, lo, hi);
+    scan_span<kSegVec>(sp, NoPre{}, [&](u32x4 b, uint32_t i0) {
+        bool pc[4], pq[4];
+        uint64_t mc[4], mq[4];
+        uint32_t tc = 0, tq = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool v = b[u] != kNoElem;
+            const uint32_t c = coarse_of_bits(b[u]);
+            pc[u] = v && c < tau;
+            pq[u] = v && c == tau;
+            mc[u] = __ballot(pc[u]);
+            mq[u] = __ballot(pq[u]);
+            tc += __builtin_popcountll(mc[u]);
+            tq += __builtin_popcountll(mq[u]);
+        }
+        if (tc + tq == 0) return;
+        if (sc_n + sq_n + tc + tq > static_cast<uint32_t>(kWaveCap)) flush();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (pc[u]) stg[mbcnt_from(mc[u], sc_n)] = make_uint2(i0 + u, 0u);
+            sc_n += __builtin_popcountll(mc[u]);
+            if (pq[u]) stg[kWaveCap - 1 - mbcnt_from(mq[u], sq_n)] = make_uint2(i0 + u, desc_key(b[u]));
+            sq_n += __builtin_popcountll(mq[u]);
+        }
+    });
+    flush();
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvx_finish_kernel(Params p) {
+    __shared__ Shared sm;
+    const uint32_t row = kvx_row();
+    if (row >= static_cast<uint32_t>(p.m_cap)) return;
+    const int32_t nvr = *p.num_valid_rows;
+    const int32_t ke_row = p.ke[row];
+    if (row >= clamp_len(nvr, p.m_cap)) return;
+    const uint32_t k = p.k;
+    if (clamp_len(ke_row, p.n) <= k) return;
+    const uint32_t before = kv_counts(p, row)[1];
+    uint32_t* ctr = kvx_ctr(p, row);
+    const uint32_t nq = ctr[1];
+    uint32_t* h0 = sm.hist[0];
+    uint32_t* h1 = sm.hist[1];
+    clear_hist(h1);
+    if (threadIdx.x == 0) {
+        sm.kext[0] = kNoElem;
+        sm.kext[1] = 0;
+    }
+    __syncthreads();  // every thread has read the counters
+    if (threadIdx.x == 0) {
+        ctr[0] = 0;
+        ctr[1] = 0;
+    }
+    count_route(p, TOPKF_ROUTE_EXACT_DIRECT);
+    const uint32_t kq = k - before;
+    int32_t* outp = p.out + static_cast<int64_t>(row) * k;
+    uint2* region = kv_region(p, row);
+    uint2* region2 = region + slice_len(p.n);
+    if (nq <= static_cast<uint32_t>(kBlock * kRegs)) {
+        refine_regs<kRegs, true>(
+            [&](int u, uint32_t& i, uint32_t& key) {
+                const uint32_t gi = threadIdx.x + kBlock * u;
+                if (gi >= nq) return false;
+                const uint2 t2 = region[gi];
+                i = t2.x;
+                key = t2.y;
+                return true;
+            },
+            h1, h0, kq, before, outp, k, sm);
+        return;
+    }
+    count_route(p, TOPKF_ROUTE_SPILL);
+    // A large frontier whose keys are all equal (a constant row, say) needs
+    // no refinement: any kq of its entries complete the output.
+    uint32_t mn = kNoElem, mx = 0;
+    for (uint32_t e = threadIdx.x; e < nq; e += kBlock) {
+        const uint32_t key = region[e].y;
+        mn = key < mn ? key : mn;
+        mx = key > mx ? key : mx;
+    }
+    lds_extremes(&sm.kext[0], mn, mx);
+    __syncthreads();
+    if (sm.kext[0] == sm.kext[1]) {
+        for (uint32_t j = threadIdx.x; j < kq; j += kBlock)
+            outp[before + j] = static_cast<int32_t>(region[j].x);
+        return;
+    }
+    for (uint32_t e = threadIdx.x; e < nq; e += kBlock) lds_inc(h1, region[e].y >> 21);
+    if (threadIdx.x == 0) {
+        sm.cnt[0] = nq;
+        sm.out_cnt = before;
+    }
+    __syncthreads();
+    const Frontier cur{sm.front, 0, region, &sm.cnt[0]};
+    const Frontier nxt{sm.front, kFront, region2, &sm.cnt[1]};
+    refine(cur, nxt, h1, h0, kq, outp, k, sm);
+}
+
 // Plain streaming read of nvec 16-byte vectors, the same 128-bit nontemporal
 // loads as the selector's scan, four per thread in flight, folded into an
 // XOR that is stored only if it equals an improbable value (so the loads
@@ -1787,8 +2041,6 @@ __global__ void coarse_keys_kernel(const float* x, int64_t n, uint16_t* out) {
 }
 
 // ------------------------------------------------------------------ host
-
-constexpr int64_t kCounterHead = 64;  // u32 slots: [0] queue, [1] exit, rest reserved
 
 struct DeviceInfo {
     int cus = 0;
@@ -1908,6 +2160,8 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
 
 void plan_sizes(const topkf_plan& pl, int64_t m_cap, int64_t n, size_t* cb, size_t* wb) {
     *cb = static_cast<size_t>(kCounterHead + 2 * m_cap) * sizeof(uint32_t);
+    if (pl.family == TOPKF_FAMILY_KVSPLIT && pl.stride == 0)
+        *cb += static_cast<size_t>(m_cap) * kBins * sizeof(uint32_t);  // per-row coarse histograms
     const size_t per_owner = 2 * static_cast<size_t>(slice_len(n)) * sizeof(uint2);
     if (pl.family == TOPKF_FAMILY_PERSISTENT) {
         // two (index, key) slices per worker: wave spills, contiguous frontier
@@ -1925,14 +2179,26 @@ hipError_t launch_family(const topkf_plan& pl, const Params& prm, hipStream_t st
         hipLaunchKernelGGL((persistent_kernel<S, D>), dim3(pl.workers), dim3(kBlock), 0, st, prm);
     } else {
         const int64_t total = static_cast<int64_t>(prm.m_cap) * pl.splits;
-        const int64_t per_xcd = (total + 7) / 8;
-        hipLaunchKernelGGL((kvsplit_scan_kernel<S, D>), dim3(static_cast<uint32_t>(per_xcd * 8)),
-                           dim3(kBlock), 0, st, prm);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const int64_t rows_per_xcd = (static_cast<int64_t>(prm.m_cap) + 7) / 8;
-        hipLaunchKernelGGL((kvsplit_finish_kernel<S, D>),
-                           dim3(static_cast<uint32_t>(rows_per_xcd * 8)), dim3(kBlock), 0, st, prm);
+        const dim3 parts(static_cast<uint32_t>((total + 7) / 8 * 8));
+        const dim3 rows(static_cast<uint32_t>((static_cast<int64_t>(prm.m_cap) + 7) / 8 * 8));
+        if constexpr (S == 0) {
+            // No view: the cooperative exact route.
+            hipLaunchKernelGGL(kvx_hist_kernel, parts, dim3(kBlock), 0, st, prm);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kvx_cut_kernel, rows, dim3(kBlock), 0, st, prm);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kvx_classify_kernel, parts, dim3(kBlock), 0, st, prm);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kvx_finish_kernel, rows, dim3(kBlock), 0, st, prm);
+        } else {
+            hipLaunchKernelGGL((kvsplit_scan_kernel<S, D>), parts, dim3(kBlock), 0, st, prm);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((kvsplit_finish_kernel<S, D>), rows, dim3(kBlock), 0, st, prm);
+        }
     }
     return hipGetLastError();
 }

@@ -273,3 +273,47 @@ def test_small_boundary_group_with_ties():
         note("small boundary group plan %s" % name)
         out, _, _ = run_topk(x, ke, k, plan=plan)
         assert_exact(out, x, ke, k)
+
+
+def test_cooperative_exact_route():
+    """KV-split without a view: each part histograms its segment, the row's
+    histograms merge in the counter buffer, the parts commit and collect the
+    boundary bin, one workgroup per row refines.  Long i.i.d., ascending,
+    constant and tied rows, short and sentinel rows, clamped live rows; the
+    counters (including the merged histograms) must be zero after each call,
+    and a second call on the same buffers must be exact too."""
+    import torch
+    from tests.gpu_util import dev
+    t = topkf()
+    k, n = 2048, 300000
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((8, n), dtype=np.float32)
+    x[1] = np.sort(x[1])                                   # tail in the last segment
+    x[2] = np.float32(0.75)                                # every value tied
+    x[3] = np.round(x[3] * 4).astype(np.float32) / 4       # heavy ties
+    x[4, rng.choice(n, 5000, replace=False)] = np.inf      # +inf flood beyond K
+    ke = np.array([n, n - 7, 250000, n, 123457, 3000, 1500, n], dtype=np.int32)
+    for name, plan in (("kvx-p8", t.make_plan(t.FAMILY_KVSPLIT, 0, 0, splits=8, min_segment=4096)),
+                       ("kvx-p32", t.make_plan(t.FAMILY_KVSPLIT, 0, 0, splits=32, min_segment=8192)),
+                       ("kvx-p3", t.make_plan(t.FAMILY_KVSPLIT, 0, 0, splits=3, min_segment=1024))):
+        note("cooperative exact route plan %s" % name)
+        out, st, _ = run_topk(x, ke, k, plan=plan, stats=True)
+        assert_exact(out, x, ke, k)
+        assert st["exact_direct"] == 7 and st["sentinel"] == 1, st   # ke = 1500 <= K
+        out, st, _ = run_topk(x, ke, k, m_live=5, plan=plan, stats=True)
+        assert_exact(out, x, ke, k, m_live=5)
+    # Two calls on one set of buffers, the second with other rows.
+    plan = t.make_plan(t.FAMILY_KVSPLIT, 0, 0, splits=16, min_segment=4096)
+    d = dev()
+    sel = t.Selector(8, n, device=d, plan=plan)
+    for trial in range(2):
+        xt = x if trial == 0 else rng.standard_normal((8, n), dtype=np.float32)
+        xd = torch.from_numpy(xt).to(d)
+        ke_d = torch.from_numpy(ke).to(d)
+        o = torch.full((8, k), -7, dtype=torch.int32, device=d)
+        nvr = torch.tensor([8], dtype=torch.int32, device=d)
+        note("cooperative exact route reuse, call %d" % trial)
+        sel(xd, ke_d, o, nvr, k)
+        torch.cuda.synchronize()
+        assert int(sel.counters.sum().item()) == 0
+        assert_exact(o.cpu().numpy(), xt, ke, k)
