@@ -93,6 +93,7 @@ struct alignas(16) Shared {
     uint32_t part_max;  // KV-split finisher: the largest candidate count of one part
     uint32_t kext[2];  // smallest and largest key of a large frontier
     uint32_t small_n;  // register refinement: entries in the small boundary list
+    uint32_t spilled;  // KV-split scan: some wave wrote candidates past its stage
 };
 static_assert(sizeof(Shared) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
@@ -1361,8 +1362,16 @@ __device__ __forceinline__ uint2* kv_region(const Params& p, uint32_t row) {
     return p.ws + 2 * static_cast<int64_t>(row) * slice_len(p.n);
 }
 
+// Per row, two words per part: its primary and band candidate counts.
 __device__ __forceinline__ uint32_t* kv_counts(const Params& p, uint32_t row) {
     return reinterpret_cast<uint32_t*>(p.ws + 2 * static_cast<int64_t>(p.m_cap) * slice_len(p.n)) +
+           2 * static_cast<int64_t>(row) * p.splits;
+}
+
+// After every row's counts, two words per part: the smallest and largest key
+// among its primary candidates (read only for frontiers beyond registers).
+__device__ __forceinline__ uint32_t* kv_ext(const Params& p, uint32_t row) {
+    return kv_counts(p, 0) + 2 * static_cast<int64_t>(p.m_cap) * p.splits +
            2 * static_cast<int64_t>(row) * p.splits;
 }
 
@@ -1434,6 +1443,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     // writes the rest straight to its reserved slots.
     uint2* stg = sm.front + wave() * kWaveCap;
     uint32_t sp_n = 0, sb_n = 0;
+    uint32_t pmin = kNoElem, pmax = 0;  // keys of primary candidates written directly
+    bool wspill = false;
     uint32_t vb[kSampleVec];
     const Span sp = make_span(x, lo, hi);
     scan_span<kSegVec>(
@@ -1441,7 +1452,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         [&]() { view_batch(x, g.a, g.nv, S, 0u, vb); },
         [&]() {
             clear_hist(h0);
-            if (threadIdx.x == 0) { sm.cnt[0] = 0; sm.cnt[1] = 0; }
+            if (threadIdx.x == 0) {
+                sm.cnt[0] = 0;
+                sm.cnt[1] = 0;
+                sm.kext[0] = kNoElem;
+                sm.kext[1] = 0;
+                sm.spilled = 0;
+            }
             __syncthreads();
             const Cuts c = phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
             T0 = c.t0;
@@ -1491,10 +1508,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                     if (pr[u]) {
                         const uint32_t slot = base + mbcnt(m[u]);
                         region[kind ? hi - 1 - slot : lo + slot] = make_uint2(i0 + u, key[u]);
+                        if (kind == 0) {
+                            pmin = key[u] < pmin ? key[u] : pmin;
+                            pmax = key[u] > pmax ? key[u] : pmax;
+                        }
                     }
                     base += __builtin_popcountll(m[u]);
                 }
             };
+            wspill = true;
             emit(pp, 0);
             if (DUAL) emit(pb, 1);
         },
@@ -1516,6 +1538,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             const uint2 v = stg[e];
             region[lo + pbase + e] = v;
         }
+        if (wspill && lane() == 0) sm.spilled = 1;
         if (DUAL) {
             for (uint32_t e = lane(); e < sb_n; e += 64) {
                 const uint2 v = stg[kWaveCap - 1 - e];
@@ -1524,10 +1547,27 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         }
     }
     __syncthreads();
+    // A part whose candidates overflowed its stage (a row whose tail is most
+    // of the row) also publishes the key range of its primary candidates, so
+    // that the finisher can recognise a tail of equal keys without reading
+    // it; any other part publishes the empty-knowledge range [0, kNoElem].
+    const bool heavy = sm.spilled != 0;
+    if (heavy) {
+        for (uint32_t e = lane(); e < sp_n; e += 64) {
+            const uint32_t key = stg[e].y;
+            pmin = key < pmin ? key : pmin;
+            pmax = key > pmax ? key : pmax;
+        }
+        lds_extremes(&sm.kext[0], pmin, pmax);
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
         uint32_t* counts = kv_counts(p, row);
         counts[2 * part] = sm.cnt[0];
         counts[2 * part + 1] = sm.cnt[1];
+        uint32_t* ext = kv_ext(p, row);
+        ext[2 * part] = heavy ? sm.kext[0] : 0u;
+        ext[2 * part + 1] = heavy ? sm.kext[1] : kNoElem;
     }
 }
 
@@ -1654,43 +1694,59 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             h1, h0, k, 0u, outp, k, sm);
         return;
     }
-    // Large frontier.  First the key extremes of the candidates in use, read
-    // range by range with several loads in flight: when every candidate
-    // carries the same key (a constant row, say), no value outside them
-    // ranks above it, so any K of them are the answer and refinement has
-    // nothing to separate; the first K in offset order are taken.
+    // Large frontier.  When every candidate carries the same key (a constant
+    // row, say), no value outside them ranks above it, so any K of them are
+    // the answer and refinement has nothing to separate; the first K in
+    // offset order are taken.  On the primary route the parts' published key
+    // extremes decide this; with the band, the extremes are read from the
+    // candidates, range by range with several loads in flight.
     {
+        uint32_t kmn = kNoElem, kmx = 0;
+        if (threadIdx.x < Pr) {
+            const uint32_t* ext = kv_ext(p, row);
+            kmn = ext[2 * threadIdx.x];
+            kmx = ext[2 * threadIdx.x + 1];
+        }
         if (threadIdx.x == 0) { sm.kext[0] = kNoElem; sm.kext[1] = 0; }
         __syncthreads();
-        uint32_t mn = kNoElem, mx = 0;
-        const int kinds = route == TOPKF_ROUTE_BAND ? 2 : 1;
-        for (int kind = 0; kind < kinds; ++kind) {
-            for (uint32_t pp = 0; pp < Pr; ++pp) {
-                const uint32_t c = sm.offs[kind][pp + 1] - sm.offs[kind][pp];
-                const uint32_t s0 = pp * chunk;
-                const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
-                for (uint32_t j0 = 0; j0 < c; j0 += 8 * kBlock) {
-                    uint32_t kk[8];
+        lds_extremes(&sm.kext[0], kmn, kmx);  // the parts' published key ranges
+        __syncthreads();
+        bool tied = route == TOPKF_ROUTE_PRIMARY && sm.kext[0] == sm.kext[1];
+        if (!tied) {
+            __syncthreads();  // every thread has read the published extremes
+            if (threadIdx.x == 0) { sm.kext[0] = kNoElem; sm.kext[1] = 0; }
+            __syncthreads();
+            uint32_t mn = kNoElem, mx = 0;
+            const int kinds = route == TOPKF_ROUTE_BAND ? 2 : 1;
+            for (int kind = 0; kind < kinds; ++kind) {
+                for (uint32_t pp = 0; pp < Pr; ++pp) {
+                    const uint32_t c = sm.offs[kind][pp + 1] - sm.offs[kind][pp];
+                    const uint32_t s0 = pp * chunk;
+                    const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
+                    for (uint32_t j0 = 0; j0 < c; j0 += 8 * kBlock) {
+                        uint32_t kk[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const uint32_t j = j0 + u * kBlock + threadIdx.x;
-                        kk[u] = kNoElem;
-                        if (j < c) kk[u] = nt_load2(region + (kind ? s1 - 1 - j : s0 + j)).y;
-                    }
+                        for (int u = 0; u < 8; ++u) {
+                            const uint32_t j = j0 + u * kBlock + threadIdx.x;
+                            kk[u] = kNoElem;
+                            if (j < c) kk[u] = nt_load2(region + (kind ? s1 - 1 - j : s0 + j)).y;
+                        }
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const uint32_t j = j0 + u * kBlock + threadIdx.x;
-                        if (j < c) {
-                            mn = kk[u] < mn ? kk[u] : mn;
-                            mx = kk[u] > mx ? kk[u] : mx;
+                        for (int u = 0; u < 8; ++u) {
+                            const uint32_t j = j0 + u * kBlock + threadIdx.x;
+                            if (j < c) {
+                                mn = kk[u] < mn ? kk[u] : mn;
+                                mx = kk[u] > mx ? kk[u] : mx;
+                            }
                         }
                     }
                 }
             }
+            lds_extremes(&sm.kext[0], mn, mx);
+            __syncthreads();
+            tied = sm.kext[0] == sm.kext[1];
         }
-        lds_extremes(&sm.kext[0], mn, mx);
-        __syncthreads();
-        if (sm.kext[0] == sm.kext[1]) {
+        if (tied) {
             for (uint32_t gi = threadIdx.x; gi < k; gi += kBlock) {
                 const int kind = gi < C0 ? 0 : 1;
                 const uint32_t r = kind ? gi - C0 : gi;
@@ -2169,7 +2225,7 @@ void plan_sizes(const topkf_plan& pl, int64_t m_cap, int64_t n, size_t* cb, size
     } else {
         // per row: part ranges and contiguous frontier, then two counts per part
         *wb = static_cast<size_t>(m_cap) *
-              (per_owner + 2 * static_cast<size_t>(pl.splits) * sizeof(uint32_t));
+              (per_owner + 4 * static_cast<size_t>(pl.splits) * sizeof(uint32_t));
     }
 }
 
