@@ -106,12 +106,12 @@ def test_workspace_sizes_follow_the_plan():
     assert wb == 10 * 2 * sl * 8         # two slices per worker
     kv = topkf.make_plan(topkf.FAMILY_KVSPLIT, 64, 0, splits=8)
     cb, wb = topkf.plan_workspace_size(kv, 5, n)
-    assert wb == 5 * (2 * sl * 8 + 2 * 8 * 4)  # two slices per row, two counts per part
+    assert wb == 5 * (2 * sl * 8 + 4 * 8 * 4)  # two slices per row, four words per part
     assert cb == 4 * (64 + 2 * 5)
     kvx = topkf.make_plan(topkf.FAMILY_KVSPLIT, 0, 0, splits=8)   # cooperative exact route
     cb, wb = topkf.plan_workspace_size(kvx, 5, n)
     assert cb == 4 * (64 + 2 * 5 + 5 * 2048)  # plus one coarse histogram per row
-    assert wb == 5 * (2 * sl * 8 + 2 * 8 * 4)
+    assert wb == 5 * (2 * sl * 8 + 4 * 8 * 4)
     for bad in (topkf.make_plan(7, 128), topkf.make_plan(1, 32), topkf.make_plan(1, 64, dual=2),
                 topkf.make_plan(1, 64, workers=0), topkf.make_plan(2, 64, splits=0),
                 topkf.make_plan(2, 64, splits=257),
