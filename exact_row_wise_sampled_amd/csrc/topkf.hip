@@ -76,7 +76,17 @@ struct Params {
     int32_t min_seg;
     int32_t band_q;  // secondary target K~1 = ceil(band_q * K / 4)
     int32_t prim_q;  // primary target K~ = ceil(prim_q * K / 4)
+    const float* hint;  // per-row proposed cutoffs (NaN: none), or null
 };
+
+// A row's caller-supplied proposal (a cutoff carried over from the previous
+// decode step, as in the GVR page): when it is not NaN, its descending key
+// replaces the view's cutoff.
+__device__ __forceinline__ bool row_hint(const Params& p, uint32_t row, uint32_t* key) {
+    const uint32_t b = __float_as_uint(p.hint[row]);
+    *key = b ^ ((~static_cast<uint32_t>(static_cast<int32_t>(b) >> 31)) >> 1);
+    return (b & 0x7FFFFFFFu) <= 0x7F800000u;
+}
 
 struct alignas(16) Shared {
     uint32_t hist[2][kBins];
@@ -1174,7 +1184,7 @@ __device__ __forceinline__ int publish_ticket(const Params& p, uint32_t t, int m
 // published at the end of Phase 1, its length is read while this row streams, and
 // its first batch of view samples is loaded when this row is done; nr.row <
 // 0 means the next row is not known yet.
-template <int S, bool DUAL>
+template <int S, bool DUAL, bool HINT>
 __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t L, bool looked,
                                               const uint32_t (&vb)[kSampleVec], uint32_t t,
                                               int m_live, Shared& sm, uint2* sliceA,
@@ -1204,7 +1214,10 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
         uint32_t a;
         const uint32_t nv = view_size<S>(row, L, &a);
         const uint32_t q = q_primary(k, S, p.prim_q), q1 = DUAL ? q_secondary(k, S, p.band_q) : q;
-        if (nv >= q1) {
+        uint32_t hkey = 0;
+        bool hinted = false;
+        if constexpr (HINT) hinted = row_hint(p, static_cast<uint32_t>(row), &hkey);
+        if (hinted || nv >= q1) {
             uint32_t T0 = 0, T1 = 0;
             int32_t ke_next = 0;
             bool on = false;
@@ -1216,9 +1229,14 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                     clear_hist(h0);
                     if (threadIdx.x == 0) sm.out_cnt = 0;
                     __syncthreads();
-                    const Cuts c = phase1(x, a, nv, S, q, q1, h0, sm, looked ? vb : nullptr);
-                    T0 = c.t0;
-                    T1 = c.t1;
+                    if (hinted) {
+                        T0 = hkey;  // the proposal replaces Phase 1; no band
+                        T1 = hkey;
+                    } else {
+                        const Cuts c = phase1(x, a, nv, S, q, q1, h0, sm, looked ? vb : nullptr);
+                        T0 = c.t0;
+                        T1 = c.t1;
+                    }
                     // The next row, drawn when this row started, is published
                     // now: the draw's latency hid behind Phase 1.
                     if (threadIdx.x == 0) publish_ticket(p, t, m_live, sm);
@@ -1232,7 +1250,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                     nr.L = nr.row < m_live ? clamp_len(ke_next, p.n) : 0u;
                     if (nr.L > k) {
                         nnv = view_size<S>(static_cast<uint32_t>(nr.row), nr.L, &na);
-                        on = nnv >= q1;
+                        on = !HINT && nnv >= q1;  // hinted launches load views inline
                         xn = p.logits + static_cast<int64_t>(nr.row) * p.stride;
                     }
                 });
@@ -1251,6 +1269,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                 }
             }
             certified = C >= k;
+            if (hinted) count_route(p, TOPKF_ROUTE_HINTED);
         }
     }
     uint32_t kq = k;
@@ -1276,7 +1295,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     return nr;
 }
 
-template <int S, bool DUAL>
+template <int S, bool DUAL, bool HINT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void persistent_kernel(Params p) {
     __shared__ Shared sm;
     const int m_live = static_cast<int>(clamp_len(*p.num_valid_rows, p.m_cap));
@@ -1296,7 +1315,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     while (row < m_live) {
         uint32_t t = 0;
         if (threadIdx.x == 0) t = atomicAdd(p.counters, 1u);
-        NextRow nr = select_row<S, DUAL>(p, row, L, looked, vb, t, m_live, sm, sliceA, sliceB);
+        NextRow nr = select_row<S, DUAL, HINT>(p, row, L, looked, vb, t, m_live, sm, sliceA, sliceB);
         if (nr.row < 0) {  // routes without a view publish the ticket here
             if (threadIdx.x == 0) publish_ticket(p, t, m_live, sm);
             __syncthreads();
@@ -1399,7 +1418,7 @@ __device__ __forceinline__ void kv_exact_row(const Params& p, const RowGeom& g, 
     finish_waves(C, region, wsl, region2, region, sm.hist[1], sm.hist[0], kq, outp, k, sm);
 }
 
-template <int S, bool DUAL>
+template <int S, bool DUAL, bool HINT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvsplit_scan_kernel(Params p) {
     __shared__ Shared sm;
     const uint32_t P = static_cast<uint32_t>(p.splits);
@@ -1410,6 +1429,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     // Both loads in flight at once (ke has M_cap entries).
     const int32_t nvr = *p.num_valid_rows;
     const int32_t ke_row = p.ke[row];
+    uint32_t hkey = 0;
+    bool hinted = false;
+    if constexpr (HINT) hinted = row_hint(p, row, &hkey);
     const uint32_t m_live = clamp_len(nvr, p.m_cap);
     if (row >= m_live) return;
     const uint32_t k = p.k;
@@ -1421,7 +1443,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         }
         return;
     }
-    if (!g.usable) {
+    if (!g.usable && !hinted) {
         // No usable view: part 0 runs the exact coarse route over the whole row.
         if (part == 0) kv_exact_row(p, g, TOPKF_ROUTE_EXACT_DIRECT, sm);
         return;
@@ -1449,7 +1471,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     const Span sp = make_span(x, lo, hi);
     scan_span<kSegVec>(
         sp,
-        [&]() { view_batch(x, g.a, g.nv, S, 0u, vb); },
+        [&]() {
+            if (!hinted) view_batch(x, g.a, g.nv, S, 0u, vb);
+        },
         [&]() {
             clear_hist(h0);
             if (threadIdx.x == 0) {
@@ -1460,9 +1484,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 sm.spilled = 0;
             }
             __syncthreads();
-            const Cuts c = phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
-            T0 = c.t0;
-            T1 = c.t1;
+            if (hinted) {
+                T0 = hkey;  // the proposal replaces Phase 1; no band
+                T1 = hkey;
+            } else {
+                const Cuts c = phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
+                T0 = c.t0;
+                T1 = c.t1;
+            }
         },
         [&](u32x4 b, uint32_t i0) {
             uint32_t key[4];
@@ -1571,7 +1600,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     }
 }
 
-template <int S, bool DUAL>
+template <int S, bool DUAL, bool HINT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void kvsplit_finish_kernel(Params p) {
     __shared__ Shared sm;
     // same XCD as the row's parts in kvsplit_scan_kernel
@@ -1583,6 +1612,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     // are dropped below.
     const int32_t nvr = *p.num_valid_rows;
     const int32_t ke_row = p.ke[row];
+    uint32_t hkey = 0;
+    bool hinted = false;
+    if constexpr (HINT) hinted = row_hint(p, row, &hkey);
     const uint32_t* counts = kv_counts(p, row);
     uint32_t cp = 0, cb = 0;
     if (threadIdx.x < static_cast<uint32_t>(p.splits)) {
@@ -1593,7 +1625,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     if (row >= m_live) return;
     const uint32_t k = p.k;
     const RowGeom g = kv_geom<S, DUAL>(p, row, ke_row);
-    if (g.L <= k || !g.usable) return;  // finished by the scan kernel
+    if (g.L <= k || (!g.usable && !hinted)) return;  // finished by the scan kernel
+    if (hinted) count_route(p, TOPKF_ROUTE_HINTED);
     const uint32_t L = g.L, Pr = g.Pr, chunk = g.chunk;
     int32_t* outp = p.out + static_cast<int64_t>(row) * k;
     uint2* region = kv_region(p, row);
@@ -2116,7 +2149,7 @@ topkf_status device_info(DeviceInfo* out) {
             cus <= 0)
             return TOPKF_EHIP;
         int occ = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, persistent_kernel<128, true>, kBlock,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, persistent_kernel<128, true, false>, kBlock,
                                                          0) != hipSuccess ||
             occ <= 0)
             occ = 1;
@@ -2229,10 +2262,10 @@ void plan_sizes(const topkf_plan& pl, int64_t m_cap, int64_t n, size_t* cb, size
     }
 }
 
-template <int S, bool D>
+template <int S, bool D, bool H>
 hipError_t launch_family(const topkf_plan& pl, const Params& prm, hipStream_t st) {
     if (pl.family == TOPKF_FAMILY_PERSISTENT) {
-        hipLaunchKernelGGL((persistent_kernel<S, D>), dim3(pl.workers), dim3(kBlock), 0, st, prm);
+        hipLaunchKernelGGL((persistent_kernel<S, D, H>), dim3(pl.workers), dim3(kBlock), 0, st, prm);
     } else {
         const int64_t total = static_cast<int64_t>(prm.m_cap) * pl.splits;
         const dim3 parts(static_cast<uint32_t>((total + 7) / 8 * 8));
@@ -2250,10 +2283,10 @@ hipError_t launch_family(const topkf_plan& pl, const Params& prm, hipStream_t st
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(kvx_finish_kernel, rows, dim3(kBlock), 0, st, prm);
         } else {
-            hipLaunchKernelGGL((kvsplit_scan_kernel<S, D>), parts, dim3(kBlock), 0, st, prm);
+            hipLaunchKernelGGL((kvsplit_scan_kernel<S, D, H>), parts, dim3(kBlock), 0, st, prm);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((kvsplit_finish_kernel<S, D>), rows, dim3(kBlock), 0, st, prm);
+            hipLaunchKernelGGL((kvsplit_finish_kernel<S, D, H>), rows, dim3(kBlock), 0, st, prm);
         }
     }
     return hipGetLastError();
@@ -2262,7 +2295,8 @@ hipError_t launch_family(const topkf_plan& pl, const Params& prm, hipStream_t st
 topkf_status run(const float* logits, int64_t m_cap, int64_t n, int64_t stride,
                  const int32_t* ke, int32_t* out, const int32_t* nvr, int32_t top_k,
                  void* counters, size_t counter_bytes, void* workspace, size_t workspace_bytes,
-                 const topkf_plan* override_plan, uint32_t* stats, hipStream_t st) {
+                 const topkf_plan* override_plan, const float* hint, uint32_t* stats,
+                 hipStream_t st) {
     if (m_cap < 0 || n < 1 || stride < n || top_k < 1 || top_k > TOPKF_K_MAX)
         return TOPKF_EINVAL;
     if (n > 0x7FFFFFFF || m_cap > 0x7FFFFFFF) return TOPKF_EUNSUPPORTED;
@@ -2298,13 +2332,21 @@ topkf_status run(const float* logits, int64_t m_cap, int64_t n, int64_t stride,
     prm.min_seg = pl.min_segment;
     prm.band_q = pl.band_quarters;
     prm.prim_q = pl.primary_quarters;
+    prm.hint = hint;
+    // A proposal replaces the view's boundary; plans without a view take the
+    // exact route whatever the proposal.
+    const bool hinted = hint != nullptr && pl.stride != 0;
     hipError_t e;
     switch (pl.stride * 2 + pl.dual) {
-        case 0: case 1: e = launch_family<0, false>(pl, prm, st); break;
-        case 128: e = launch_family<64, false>(pl, prm, st); break;
-        case 129: e = launch_family<64, true>(pl, prm, st); break;
-        case 256: e = launch_family<128, false>(pl, prm, st); break;
-        default: e = launch_family<128, true>(pl, prm, st); break;
+        case 0: case 1: e = launch_family<0, false, false>(pl, prm, st); break;
+        case 128: e = hinted ? launch_family<64, false, true>(pl, prm, st)
+                             : launch_family<64, false, false>(pl, prm, st); break;
+        case 129: e = hinted ? launch_family<64, true, true>(pl, prm, st)
+                             : launch_family<64, true, false>(pl, prm, st); break;
+        case 256: e = hinted ? launch_family<128, false, true>(pl, prm, st)
+                             : launch_family<128, false, false>(pl, prm, st); break;
+        default: e = hinted ? launch_family<128, true, true>(pl, prm, st)
+                            : launch_family<128, true, false>(pl, prm, st); break;
     }
     return e == hipSuccess ? TOPKF_OK : TOPKF_EHIP;
 }
@@ -2331,7 +2373,17 @@ topkf_status topk_filtered(const float* logits, int64_t num_rows, int64_t max_kv
                            size_t counter_bytes, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
     return run(logits, num_rows, max_kv_len, row_stride, ke, out, num_valid_rows, top_k, counters,
-               counter_bytes, workspace, workspace_bytes, nullptr, nullptr, stream);
+               counter_bytes, workspace, workspace_bytes, nullptr, nullptr, nullptr, stream);
+}
+
+topkf_status topk_filtered_hinted(const float* logits, int64_t num_rows, int64_t max_kv_len,
+                                  int64_t row_stride, const int32_t* ke, int32_t* out,
+                                  const int32_t* num_valid_rows, int32_t top_k, const float* hint,
+                                  void* counters, size_t counter_bytes, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    if (num_rows > 0 && !hint) return TOPKF_EINVAL;
+    return run(logits, num_rows, max_kv_len, row_stride, ke, out, num_valid_rows, top_k, counters,
+               counter_bytes, workspace, workspace_bytes, nullptr, hint, nullptr, stream);
 }
 
 topkf_status topk_filtered_debug(const float* logits, int64_t num_rows, int64_t max_kv_len,
@@ -2341,7 +2393,19 @@ topkf_status topk_filtered_debug(const float* logits, int64_t num_rows, int64_t 
                                  const topkf_plan* plan, uint32_t* route_stats,
                                  hipStream_t stream) {
     return run(logits, num_rows, max_kv_len, row_stride, ke, out, num_valid_rows, top_k, counters,
-               counter_bytes, workspace, workspace_bytes, plan, route_stats, stream);
+               counter_bytes, workspace, workspace_bytes, plan, nullptr, route_stats, stream);
+}
+
+topkf_status topk_filtered_hinted_debug(const float* logits, int64_t num_rows,
+                                        int64_t max_kv_len, int64_t row_stride, const int32_t* ke,
+                                        int32_t* out, const int32_t* num_valid_rows, int32_t top_k,
+                                        const float* hint, void* counters, size_t counter_bytes,
+                                        void* workspace, size_t workspace_bytes,
+                                        const topkf_plan* plan, uint32_t* route_stats,
+                                        hipStream_t stream) {
+    if (num_rows > 0 && !hint) return TOPKF_EINVAL;
+    return run(logits, num_rows, max_kv_len, row_stride, ke, out, num_valid_rows, top_k, counters,
+               counter_bytes, workspace, workspace_bytes, plan, hint, route_stats, stream);
 }
 
 const char* topkf_status_string(topkf_status s) {

@@ -38,7 +38,7 @@ FAMILY_PERSISTENT = 1
 FAMILY_KVSPLIT = 2
 
 ROUTE_NAMES = ["sentinel", "primary", "band", "exact_underfill", "exact_direct", "spill",
-               "reserved6", "reserved7"]
+               "hinted", "reserved7"]
 ROUTE_COUNT = 8
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape",
@@ -68,6 +68,12 @@ _lib.topk_filtered.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, 
 _lib.topk_filtered_debug.restype = _i32
 _lib.topk_filtered_debug.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _sz, _vp,
                                      _sz, _c.POINTER(Plan), _vp, _vp]
+_lib.topk_filtered_hinted.restype = _i32
+_lib.topk_filtered_hinted.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _sz,
+                                      _vp, _sz, _vp]
+_lib.topk_filtered_hinted_debug.restype = _i32
+_lib.topk_filtered_hinted_debug.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp,
+                                            _sz, _vp, _sz, _c.POINTER(Plan), _vp, _vp]
 _lib.topkf_status_string.restype = _c.c_char_p
 _lib.topkf_status_string.argtypes = [_i32]
 _lib.topkf_plan_for.restype = _i32
@@ -157,26 +163,39 @@ def _check_tensors(logits, ke, output, num_valid_rows, top_k):
 
 
 def topk_filtered(logits, ke, output, num_valid_rows, top_k: int, counters, workspace,
-                  stream=None, plan: Plan | None = None, route_stats=None) -> None:
+                  stream=None, plan: Plan | None = None, route_stats=None, hint=None) -> None:
     """Exact row-wise Top-K of logits[r, :ke[r]] into output[r] for r < num_valid_rows.
 
     `plan` and `route_stats` (a uint32/int32 tensor of ROUTE_COUNT entries) select
-    the diagnostic entry point topk_filtered_debug.
+    the diagnostic entry points; `hint` (float32, one proposed cutoff per row,
+    NaN for none) selects topk_filtered_hinted.
     """
     _check_tensors(logits, ke, output, num_valid_rows, top_k)
     m, n = logits.shape
     row_stride = logits.stride(0) if m > 0 else n
     st = _stream_handle(stream, logits.device)
-    args = (logits.data_ptr(), m, n, row_stride, ke.data_ptr(), output.data_ptr(),
-            num_valid_rows.data_ptr(), int(top_k), counters.data_ptr(),
-            counters.numel() * counters.element_size(), workspace.data_ptr(),
+    head = (logits.data_ptr(), m, n, row_stride, ke.data_ptr(), output.data_ptr(),
+            num_valid_rows.data_ptr(), int(top_k))
+    bufs = (counters.data_ptr(), counters.numel() * counters.element_size(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size())
-    if plan is None and route_stats is None:
-        _check(_lib.topk_filtered(*args, st), "topk_filtered")
+    debug = plan is not None or route_stats is not None
+    pp = _c.byref(plan) if plan is not None else None
+    rs = route_stats.data_ptr() if route_stats is not None else None
+    if hint is not None:
+        if hint.dtype != torch.float32 or hint.dim() != 1 or hint.shape[0] != m:
+            raise TypeError("hint must be a float32 tensor with one entry per row")
+        if not hint.is_contiguous() or hint.device != logits.device:
+            raise ValueError("hint must be contiguous and on the device of logits")
+        if debug:
+            _check(_lib.topk_filtered_hinted_debug(*head, hint.data_ptr(), *bufs, pp, rs, st),
+                   "topk_filtered_hinted_debug")
+        else:
+            _check(_lib.topk_filtered_hinted(*head, hint.data_ptr(), *bufs, st),
+                   "topk_filtered_hinted")
+    elif debug:
+        _check(_lib.topk_filtered_debug(*head, *bufs, pp, rs, st), "topk_filtered_debug")
     else:
-        pp = _c.byref(plan) if plan is not None else None
-        rs = route_stats.data_ptr() if route_stats is not None else None
-        _check(_lib.topk_filtered_debug(*args, pp, rs, st), "topk_filtered_debug")
+        _check(_lib.topk_filtered(*head, *bufs, st), "topk_filtered")
 
 
 def coarse_keys(x, out, stream=None) -> None:
@@ -217,6 +236,7 @@ class Selector:
         self.counters = torch.zeros(max(cb, 1), dtype=torch.uint8, device=device)
         self.workspace = torch.empty(max(wb, 1), dtype=torch.uint8, device=device)
 
-    def __call__(self, logits, ke, output, num_valid_rows, top_k, stream=None, route_stats=None):
+    def __call__(self, logits, ke, output, num_valid_rows, top_k, stream=None, route_stats=None,
+                 hint=None):
         topk_filtered(logits, ke, output, num_valid_rows, top_k, self.counters, self.workspace,
-                      stream=stream, plan=self.plan, route_stats=route_stats)
+                      stream=stream, plan=self.plan, route_stats=route_stats, hint=hint)

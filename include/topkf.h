@@ -157,6 +157,8 @@ topkf_status topkf_plan_workspace_size(const topkf_plan* plan, int64_t num_rows,
 #define TOPKF_ROUTE_EXACT_UNDERFILL 3 /* exact coarse recovery after underfill */
 #define TOPKF_ROUTE_EXACT_DIRECT 4   /* exact coarse route: no view or unusable view */
 #define TOPKF_ROUTE_SPILL 5          /* rows whose frontier overflowed on-chip storage */
+#define TOPKF_ROUTE_HINTED 6         /* rows whose caller-supplied proposal replaced the view
+                                        (counted in addition to the route they took) */
 #define TOPKF_ROUTE_COUNT 8
 
 /*
@@ -173,6 +175,37 @@ topkf_status topk_filtered_debug(const float* logits, int64_t num_rows, int64_t 
                                  size_t counter_bytes, void* workspace, size_t workspace_bytes,
                                  const topkf_plan* plan, uint32_t* route_stats,
                                  hipStream_t stream);
+
+/*
+ * topk_filtered with a caller-supplied proposal per row, as the GVR page
+ * carries a threshold over from the previous decode step (its Sec. "Core
+ * claim"; the paper's Sec. 2.2 "History-dependent prediction").
+ *   hint  device, float[M_cap]: row r admits every valid value >= hint[r]
+ *         (compared as descending keys, so +0 ranks above -0) in place of the
+ *         boundary its view would propose; NaN means no proposal and the row
+ *         uses its view.  A proposal is never trusted: the complete-row count
+ *         certifies it, and a row it underfills takes the exact coarse route
+ *         (no secondary band), so the result is exact for any hint.  A useful
+ *         hint admits a little more than K values (e.g. the previous step's
+ *         value near rank 1.25K); plans without a view ignore hints.
+ * Other arguments, errors and buffers as topk_filtered; TOPKF_EINVAL also for
+ * a null hint with num_rows > 0.
+ */
+topkf_status topk_filtered_hinted(const float* logits, int64_t num_rows, int64_t max_kv_len,
+                                  int64_t row_stride, const int32_t* ke, int32_t* out,
+                                  const int32_t* num_valid_rows, int32_t top_k, const float* hint,
+                                  void* counters, size_t counter_bytes, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* topk_filtered_hinted with an explicit plan and route statistics (as
+ * topk_filtered_debug). */
+topkf_status topk_filtered_hinted_debug(const float* logits, int64_t num_rows,
+                                        int64_t max_kv_len, int64_t row_stride, const int32_t* ke,
+                                        int32_t* out, const int32_t* num_valid_rows, int32_t top_k,
+                                        const float* hint, void* counters, size_t counter_bytes,
+                                        void* workspace, size_t workspace_bytes,
+                                        const topkf_plan* plan, uint32_t* route_stats,
+                                        hipStream_t stream);
 
 /*
  * The 11-bit coarse key of paper Sec. 4.2, Eq. 11, for n device floats:

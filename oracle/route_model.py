@@ -38,6 +38,13 @@ in the scan (Sec. 5.3) is, by the pages' own argument, the same predicate as
 c(x) <= tau, so this model counts with c(x) directly.
 
 Rows of length L <= K take the sentinel layout (Sec. 2.1).
+
+A caller-supplied proposal (a cutoff carried over from the previous decode
+step, the GVR page's temporal guess) replaces the view's boundary in a plan
+that has a view: the row admits every value whose descending key is at most
+the proposal's, certifies it by the same complete-row count, and on underfill
+goes to exact coarse recovery (there is no secondary boundary).  A NaN
+proposal means none.
 """
 from __future__ import annotations
 
@@ -58,6 +65,14 @@ def coarse_keys(x: np.ndarray) -> np.ndarray:
         h = np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
     k16 = np.where(h & 0x8000, h, h ^ 0x7FFF)
     return (k16 >> 5).astype(np.int64)
+
+
+def desc_keys(x: np.ndarray) -> np.ndarray:
+    """Descending sortable keys of float32 values: the bit pattern with every
+    bit but the sign flipped when the sign is clear, as is when set, so a
+    larger value gets a smaller key and +0 ranks above -0."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return np.where(b & 0x80000000, b, b ^ 0x7FFFFFFF).astype(np.int64)
 
 
 def row_phase(r: int, s: int) -> int:
@@ -97,6 +112,7 @@ class RowRoute:
     tau1: int = -1
     c0: int = 0   # C(tau0)
     c1: int = 0   # C(tau1) (equal to c0 without a secondary boundary)
+    hinted: bool = False  # a proposal replaced the view
 
 
 def first_bin_reaching(hist: np.ndarray, target: int) -> int:
@@ -104,12 +120,20 @@ def first_bin_reaching(hist: np.ndarray, target: int) -> int:
     return int(np.searchsorted(np.cumsum(hist), target, side="left"))
 
 
-def route_row(x_row: np.ndarray, L: int, r: int, k: int, pol: Policy) -> RowRoute:
-    """The route row r (index within the call, length L) takes under `pol`."""
+def route_row(x_row: np.ndarray, L: int, r: int, k: int, pol: Policy,
+              hint: float | None = None) -> RowRoute:
+    """The route row r (index within the call, length L) takes under `pol`,
+    with an optional proposed cutoff `hint` (NaN or None: no proposal)."""
     if L <= k:
         return RowRoute("sentinel", L)
     if pol.stride == 0:
         return RowRoute("exact_direct", L)
+    if hint is not None and not np.isnan(hint):
+        hk = int(desc_keys(np.array([hint], dtype=np.float32))[0])
+        c0 = int(np.count_nonzero(desc_keys(x_row[:L]) <= hk))
+        rr = RowRoute("primary" if c0 >= k else "exact_underfill", L, c0=c0, c1=c0)
+        rr.hinted = True
+        return rr
     s = pol.stride
     a = row_phase(r, s)
     view = x_row[a:L:s]
@@ -133,16 +157,21 @@ def route_row(x_row: np.ndarray, L: int, r: int, k: int, pol: Policy) -> RowRout
     return rr
 
 
-def route_rows(x: np.ndarray, ke, k: int, pol: Policy, m_live: int | None = None):
+def route_rows(x: np.ndarray, ke, k: int, pol: Policy, m_live: int | None = None, hints=None):
     """Per-row routes of rows r < min(m_live, M); lengths clamped to [0, N]."""
     m, n = x.shape
     live = m if m_live is None else max(0, min(int(m_live), m))
     ke = np.asarray(ke)
-    return [route_row(x[r], int(min(max(int(ke[r]), 0), n)), r, k, pol) for r in range(live)]
+    return [route_row(x[r], int(min(max(int(ke[r]), 0), n)), r, k, pol,
+                      None if hints is None else float(hints[r])) for r in range(live)]
 
 
-def route_counts(x: np.ndarray, ke, k: int, pol: Policy, m_live: int | None = None) -> dict:
+def route_counts(x: np.ndarray, ke, k: int, pol: Policy, m_live: int | None = None,
+                 hints=None) -> dict:
+    """Rows per route, plus `hinted`: rows whose proposal replaced the view."""
     counts = {name: 0 for name in ROUTES}
-    for rr in route_rows(x, ke, k, pol, m_live):
+    counts["hinted"] = 0
+    for rr in route_rows(x, ke, k, pol, m_live, hints):
         counts[rr.route] += 1
+        counts["hinted"] += int(rr.hinted)
     return counts

@@ -65,15 +65,17 @@ def assert_exact(out: np.ndarray, x: np.ndarray, ke: np.ndarray, k: int, m_live=
         assert (out[res.rows:] == canary).all(), "rows >= M_live were written"
 
 
-def assert_routes(st: dict, x: np.ndarray, ke: np.ndarray, k: int, plan, m_live=None) -> dict:
+def assert_routes(st: dict, x: np.ndarray, ke: np.ndarray, k: int, plan, m_live=None,
+                  hints=None) -> dict:
     """The selector's route counters equal the CPU route model's counts for
-    every exclusive route (the spill counter is an extra, capacity-dependent
-    tally and is not modelled).  `plan` is the plan the call ran with."""
+    every exclusive route and for the rows whose proposal replaced the view
+    (the spill counter is an extra, capacity-dependent tally and is not
+    modelled).  `plan` is the plan the call ran with, `hints` its proposals."""
     from oracle import route_model as rm
     pol = rm.Policy(int(plan.stride), bool(plan.dual), int(plan.primary_quarters),
                     int(plan.band_quarters))
-    want = rm.route_counts(x, ke, k, pol, m_live=m_live)
-    got = {name: int(st[name]) for name in rm.ROUTES}
+    want = rm.route_counts(x, ke, k, pol, m_live=m_live, hints=hints)
+    got = {name: int(st[name]) for name in want}
     assert got == want, "routes: selector %s, model %s" % (got, want)
     return want
 

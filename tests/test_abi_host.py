@@ -31,7 +31,8 @@ def test_header_declares_the_api():
     names = declared_functions()
     for want in ("topk_filtered_workspace_size", "topk_filtered", "topkf_status_string",
                  "topkf_plan_for", "topkf_plan_workspace_size", "topk_filtered_debug",
-                 "topkf_coarse_keys", "topkf_read_probe", "topkf_coarse_cutoffs"):
+                 "topkf_coarse_keys", "topkf_read_probe", "topkf_coarse_cutoffs",
+                 "topk_filtered_hinted", "topk_filtered_hinted_debug"):
         assert want in names, names
 
 
@@ -121,3 +122,16 @@ def test_workspace_sizes_follow_the_plan():
                 topkf.make_plan(1, 128, 1, workers=2, primary_quarters=7, band_quarters=7)):
         with pytest.raises(topkf.TopkfError):
             topkf.plan_workspace_size(bad, 5, n)
+
+
+def test_hinted_entry_rejects_a_null_hint(lib):
+    # Argument check before any device access: a null proposal array with rows.
+    c = ctypes
+    f = lib.topk_filtered_hinted
+    f.restype = c.c_int32
+    f.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_int64, c.c_void_p, c.c_void_p,
+                  c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_size_t, c.c_void_p,
+                  c.c_size_t, c.c_void_p]
+    fake = 0x1000
+    assert f(fake, 4, 100, 100, fake, fake, fake, 8, None, fake, 1 << 20, fake, 1 << 20,
+             None) == 1

@@ -139,8 +139,9 @@ def test_counts_respect_live_rows_and_clamping():
     c = rm.route_counts(w.x, w.ke, 256, rm.Policy(64), m_live=5)
     assert sum(c.values()) == 5
     assert c["sentinel"] == 2            # ke = -3 and ke = 100
-    assert rm.route_counts(w.x, w.ke, 256, rm.Policy(64), m_live=0) == \
-        {name: 0 for name in rm.ROUTES}
+    zero = {name: 0 for name in rm.ROUTES}
+    zero["hinted"] = 0
+    assert rm.route_counts(w.x, w.ke, 256, rm.Policy(64), m_live=0) == zero
 
 
 def _view_ranks(x, L, r, s, q):
@@ -175,3 +176,38 @@ def test_view_rank_statistics_eq8():
     assert abs(hits - m * p) < 4 * math.sqrt(m * p * (1 - p)) + 2
     under = sum(rr.route != "primary" for rr in routes)
     assert under <= hits
+
+
+def test_desc_keys_order():
+    # Descending keys: larger values get smaller keys, +0 above -0, and the
+    # FP32 landmarks at their closed-form patterns.
+    v = np.array([np.inf, 3.0, 1.0, 1e-45, 0.0, -0.0, -1e-45, -1.0, -np.inf], dtype=np.float32)
+    kk = rm.desc_keys(v)
+    assert np.all(np.diff(kk) > 0)
+    assert kk[0] == 0x7F800000 ^ 0x7FFFFFFF and kk[4] == 0x7FFFFFFF and kk[5] == 0x80000000
+    assert kk[-1] == 0xFF800000
+
+
+def test_hinted_routes_closed_forms():
+    # A proposal replaces the view (plans with a view only): the row admits
+    # every value at or above it; the count certifies it or the row goes to
+    # exact recovery (no band).
+    rng = np.random.default_rng(3)
+    k, L = 256, 20000
+    x = rng.permutation(np.arange(L, dtype=np.float32) * np.float32(0.5))   # distinct values
+    vk = np.sort(x)[::-1][k - 1]
+    pol = rm.Policy(128, True, 6, 10)
+    rr = rm.route_row(x, L, 7, k, pol, float(vk))
+    assert (rr.route, rr.c0, rr.hinted) == ("primary", k, True)
+    rr = rm.route_row(x, L, 7, k, pol, float(vk) + 0.25)          # one value short
+    assert (rr.route, rr.c0) == ("exact_underfill", k - 1)
+    rr = rm.route_row(x, L, 7, k, pol, float(-np.inf))
+    assert (rr.route, rr.c0) == ("primary", L)
+    assert not rm.route_row(x, L, 7, k, pol, float("nan")).hinted   # no proposal: the view
+    assert rm.route_row(x, L, 7, k, rm.Policy(0), float(vk)).route == "exact_direct"
+    assert rm.route_row(x, k, 7, k, pol, float(vk)).route == "sentinel"
+    z = np.full(L, -0.0, dtype=np.float32)
+    z[: k + 5] = 0.0                                               # +0 ranks above -0
+    assert rm.route_row(z, L, 7, k, pol, 0.0).c0 == k + 5
+    c = rm.route_counts(np.stack([x, x]), [L, L], k, pol, hints=[float(vk), float("nan")])
+    assert c["hinted"] == 1 and c["primary"] + c["band"] + c["exact_underfill"] == 2
