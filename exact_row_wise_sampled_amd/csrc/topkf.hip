@@ -2351,6 +2351,90 @@ topkf_status run(const float* logits, int64_t m_cap, int64_t n, int64_t stride,
     return e == hipSuccess ? TOPKF_OK : TOPKF_EHIP;
 }
 
+// ------------------------------------------------------ allocation-free calls
+//
+// topk_filtered_noalloc takes its counters and workspace from one
+// library-owned device array instead of caller buffers.  Every GPU the library
+// runs on holds its own copy of the array until the process ends, and every
+// call on that GPU shares it: calls that overlap on one GPU race.  Layout:
+// the first kScratchCounterBytes are the counter buffer (zero between calls;
+// cleared once per device, then returned to zero by every call), the rest is
+// the workspace (any contents).
+constexpr size_t kScratchBytes = static_cast<size_t>(256) << 20;
+constexpr size_t kScratchCounterBytes = static_cast<size_t>(1) << 20;
+constexpr size_t kScratchWorkBytes = kScratchBytes - kScratchCounterBytes;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// A host-side handle of each device's copy of `scratch`: its device address
+// (from hipGetSymbolAddress; the array's name in host code is no device
+// address) and whether its counter part has been cleared.
+struct ScratchRef {
+    unsigned char* ptr = nullptr;
+    bool cleared = false;
+};
+ScratchRef g_scratch[64];  // guarded by g_mu
+
+__global__ __launch_bounds__(kBlock) void zero_words_kernel(uint4* p, int64_t n16) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kBlock) + threadIdx.x; i < n16;
+         i += static_cast<int64_t>(gridDim.x) * kBlock)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's scratch address; on the first call on a device the
+// counter part is cleared on `st` (a fill kernel, so that a call captured in a
+// HIP graph records no memset node).
+topkf_status scratch_for_device(hipStream_t st, unsigned char** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return TOPKF_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    ScratchRef& s = g_scratch[dev];
+    if (!s.ptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TOPKF_EHIP;
+        s.ptr = static_cast<unsigned char*>(ptr);
+    }
+    if (!s.cleared) {
+        const int64_t n16 = static_cast<int64_t>(kScratchCounterBytes / 16);
+        hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<uint32_t>(n16 / kBlock)), dim3(kBlock), 0,
+                           st, reinterpret_cast<uint4*>(s.ptr), n16);
+        if (hipGetLastError() != hipSuccess) return TOPKF_EHIP;
+        // A clear recorded into a graph under capture has not run yet: clear
+        // again on the next call.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) return TOPKF_EHIP;
+        s.cleared = cs == hipStreamCaptureStatusNone;
+    }
+    *out = s.ptr;
+    return TOPKF_OK;
+}
+
+// The automatic plan narrowed to the scratch: a plan whose workspace does not
+// fit becomes the persistent mapping with as many workers as fit.
+topkf_status noalloc_plan(int64_t m_cap, int64_t n, topkf_plan* pl) {
+    DeviceInfo di;
+    const topkf_status s = device_info(&di);
+    if (s != TOPKF_OK) return s;
+    make_plan(m_cap, n, di.cus, di.occupancy, pl);
+    size_t cb = 0, wb = 0;
+    plan_sizes(*pl, m_cap, n, &cb, &wb);
+    if (cb > kScratchCounterBytes) return TOPKF_EWORKSPACE;
+    if (wb <= kScratchWorkBytes) return TOPKF_OK;
+    if (pl->family == TOPKF_FAMILY_KVSPLIT) {
+        const int64_t pool = static_cast<int64_t>(di.cus) * di.occupancy;
+        pl->family = TOPKF_FAMILY_PERSISTENT;
+        pl->splits = 1;
+        pl->dual = pl->stride ? 1 : 0;
+        pl->primary_quarters = 7;
+        pl->workers = static_cast<int32_t>(m_cap < pool ? m_cap : pool);
+    }
+    const size_t per_worker = 2 * static_cast<size_t>(slice_len(n)) * sizeof(uint2);
+    const size_t fit = kScratchWorkBytes / per_worker;
+    if (fit < 1) return TOPKF_EWORKSPACE;
+    if (static_cast<size_t>(pl->workers) > fit) pl->workers = static_cast<int32_t>(fit);
+    return TOPKF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2384,6 +2468,27 @@ topkf_status topk_filtered_hinted(const float* logits, int64_t num_rows, int64_t
     if (num_rows > 0 && !hint) return TOPKF_EINVAL;
     return run(logits, num_rows, max_kv_len, row_stride, ke, out, num_valid_rows, top_k, counters,
                counter_bytes, workspace, workspace_bytes, nullptr, hint, nullptr, stream);
+}
+
+topkf_status topk_filtered_noalloc(const float* logits, int64_t num_rows, int64_t max_kv_len,
+                                   int64_t row_stride, const int32_t* ke, int32_t* out,
+                                   const int32_t* num_valid_rows, int32_t top_k,
+                                   hipStream_t stream) {
+    if (num_rows < 0 || max_kv_len < 1 || row_stride < max_kv_len || top_k < 1 ||
+        top_k > TOPKF_K_MAX)
+        return TOPKF_EINVAL;
+    if (max_kv_len > 0x7FFFFFFF || num_rows > 0x7FFFFFFF) return TOPKF_EUNSUPPORTED;
+    if (num_rows == 0) return TOPKF_OK;
+    if (!logits || !ke || !out || !num_valid_rows) return TOPKF_EINVAL;
+    topkf_plan pl;
+    topkf_status s = noalloc_plan(num_rows, max_kv_len, &pl);
+    if (s != TOPKF_OK) return s;
+    unsigned char* base = nullptr;
+    s = scratch_for_device(stream, &base);
+    if (s != TOPKF_OK) return s;
+    return run(logits, num_rows, max_kv_len, row_stride, ke, out, num_valid_rows, top_k, base,
+               kScratchCounterBytes, base + kScratchCounterBytes, kScratchWorkBytes, &pl, nullptr,
+               nullptr, stream);
 }
 
 topkf_status topk_filtered_debug(const float* logits, int64_t num_rows, int64_t max_kv_len,

@@ -32,6 +32,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 K_MAX = 2048
+NOALLOC_SCRATCH_BYTES = 256 << 20  # the device array of topk_filtered_noalloc
 
 FAMILY_AUTO = 0
 FAMILY_PERSISTENT = 1
@@ -74,6 +75,8 @@ _lib.topk_filtered_hinted.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32
 _lib.topk_filtered_hinted_debug.restype = _i32
 _lib.topk_filtered_hinted_debug.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp,
                                             _sz, _vp, _sz, _c.POINTER(Plan), _vp, _vp]
+_lib.topk_filtered_noalloc.restype = _i32
+_lib.topk_filtered_noalloc.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]
 _lib.topkf_status_string.restype = _c.c_char_p
 _lib.topkf_status_string.argtypes = [_i32]
 _lib.topkf_plan_for.restype = _i32
@@ -171,6 +174,15 @@ def topk_filtered(logits, ke, output, num_valid_rows, top_k: int, counters, work
     NaN for none) selects topk_filtered_hinted.
     """
     _check_tensors(logits, ke, output, num_valid_rows, top_k)
+    for name, t in (("counters", counters), ("workspace", workspace),
+                    ("route_stats", route_stats)):
+        if t is None:
+            continue
+        if t.device != logits.device or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous tensor on the device of logits" % name)
+    if route_stats is not None and (route_stats.element_size() != 4 or
+                                    route_stats.numel() < ROUTE_COUNT):
+        raise TypeError("route_stats must hold at least %d 32-bit counters" % ROUTE_COUNT)
     m, n = logits.shape
     row_stride = logits.stride(0) if m > 0 else n
     st = _stream_handle(stream, logits.device)
@@ -196,6 +208,19 @@ def topk_filtered(logits, ke, output, num_valid_rows, top_k: int, counters, work
         _check(_lib.topk_filtered_debug(*head, *bufs, pp, rs, st), "topk_filtered_debug")
     else:
         _check(_lib.topk_filtered(*head, *bufs, st), "topk_filtered")
+
+
+def topk_filtered_noalloc(logits, ke, output, num_valid_rows, top_k: int, stream=None) -> None:
+    """topk_filtered without counter and workspace arguments: the library takes
+    both from its own device array (see topk_filtered_noalloc in
+    include/topkf.h; calls that overlap on one GPU race)."""
+    _check_tensors(logits, ke, output, num_valid_rows, top_k)
+    m, n = logits.shape
+    row_stride = logits.stride(0) if m > 0 else n
+    st = _stream_handle(stream, logits.device)
+    _check(_lib.topk_filtered_noalloc(logits.data_ptr(), m, n, row_stride, ke.data_ptr(),
+                                      output.data_ptr(), num_valid_rows.data_ptr(), int(top_k),
+                                      st), "topk_filtered_noalloc")
 
 
 def coarse_keys(x, out, stream=None) -> None:

@@ -102,6 +102,35 @@ topkf_status topk_filtered(const float* logits, int64_t num_rows, int64_t max_kv
                            size_t counter_bytes, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * topk_filtered for callers that cannot allocate device memory or pass
+ * buffers: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Not part of the pages' API.
+ *
+ * Same operation, arguments, output and errors as topk_filtered, minus the
+ * counter and workspace buffers: the library takes both from one device
+ * array of TOPKF_NOALLOC_SCRATCH_BYTES (256 MiB) that it owns.  Every GPU the
+ * library runs on holds its own copy of that array until the process ends,
+ * and all calls on one GPU share it, so calls that overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race
+ * and must not be issued.  The first call on a device also enqueues a clear
+ * of the array's counter part on `stream`.  The call performs no allocation
+ * (no hipMalloc, hipFree or allocating library routine) and reads no device
+ * data on the host.
+ *
+ * Limits: the counters need (64 + 2 * num_rows) * 4 bytes of a 1 MiB counter
+ * part, so num_rows <= 131040; the workspace part holds 255 MiB.  The
+ * automatic plan is used when its workspace fits; otherwise the rows are
+ * taken by persistent workers, as many as fit at 16 * (max_kv_len + 128)
+ * bytes each.  TOPKF_EWORKSPACE when num_rows or max_kv_len exceed these
+ * limits (max_kv_len above about 16.7M columns), without launching.
+ */
+#define TOPKF_NOALLOC_SCRATCH_BYTES (256u << 20)
+topkf_status topk_filtered_noalloc(const float* logits, int64_t num_rows, int64_t max_kv_len,
+                                   int64_t row_stride, const int32_t* ke, int32_t* out,
+                                   const int32_t* num_valid_rows, int32_t top_k,
+                                   hipStream_t stream);
+
 /* Static text for a status code; never null. */
 const char* topkf_status_string(topkf_status status);
 
