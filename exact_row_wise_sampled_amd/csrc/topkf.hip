@@ -30,6 +30,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "topkf.h"
 
@@ -43,7 +44,8 @@ constexpr int kWaveCap = kFront / kWaves;    // wave-private share of it (896)
 constexpr int kWaveRegs = kWaveCap / 64;     // its entries per lane (14)
 constexpr int kRegs = 16;                    // contiguous frontier held in registers
 constexpr int kCapA = 4096;                  // general path: LDS part of Q1 / Q2
-constexpr int kRowVec = 4;      // persistent scan: 128-bit loads per thread per chunk
+constexpr int kRowVec = 4;      // exact route and band pass: 128-bit loads per thread per chunk
+constexpr int kScanVec = 6;     // persistent sampled scan: 128-bit loads per thread in flight
 constexpr int kSegVec = 8;      // KV-split scan: 128-bit loads per thread per chunk
 constexpr int kSampleVec = 8;   // view samples per thread per batch
 constexpr int kMaxSplits = 256; // KV-split parts per row
@@ -88,9 +90,9 @@ __device__ __forceinline__ bool row_hint(const Params& p, uint32_t row, uint32_t
     return (b & 0x7FFFFFFFu) <= 0x7F800000u;
 }
 
+// The scalars come first so that their LDS addresses fit the 16-bit
+// immediate offset of LDS instructions (no address registers needed).
 struct alignas(16) Shared {
-    uint32_t hist[2][kBins];
-    uint2 front[kFront];
     uint32_t offs[2][kMaxSplits + 1];  // KV-split finisher: per-part prefix offsets
     alignas(16) uint32_t wsum[3][kWaves];  // per-wave totals: [0] block_find, [1], [2] scans
     uint32_t wcnt[kWaves];             // wave-private frontier sizes
@@ -104,6 +106,8 @@ struct alignas(16) Shared {
     uint32_t kext[2];  // smallest and largest key of a large frontier
     uint32_t small_n;  // register refinement: entries in the small boundary list
     uint32_t spilled;  // KV-split scan: some wave wrote candidates past its stage
+    alignas(16) uint32_t hist[2][kBins];
+    uint2 front[kFront];
 };
 static_assert(sizeof(Shared) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
@@ -228,7 +232,11 @@ __device__ __forceinline__ uint32_t q_secondary(uint32_t k, int s, int band_q) {
 // ------------------------------------------------------------ wave helpers
 
 __device__ __forceinline__ uint32_t lane() { return __lane_id(); }
-__device__ __forceinline__ uint32_t wave() { return threadIdx.x >> 6; }
+// The wave's index in the workgroup, in a scalar register (it is the same
+// for every lane of the wave).
+__device__ __forceinline__ uint32_t wave() {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)));
+}
 
 __device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -248,6 +256,15 @@ __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
 // A value every lane holds alike, moved to a scalar register.
 __device__ __forceinline__ uint32_t readfirst(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
+// Instruction-issue priority of this wave against the other waves of its
+// SIMD: the latency-bound phases of a row (Phase 1, the end of the scan,
+// refinement) run above the streaming loop of the co-resident workgroup,
+// whose waves mostly wait on memory.
+__device__ __forceinline__ void wave_priority(int level) {
+    if (level == 0) __builtin_amdgcn_s_setprio(0);
+    else __builtin_amdgcn_s_setprio(2);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
@@ -459,38 +476,39 @@ __device__ __forceinline__ void wput(const WaveFrontier& f, uint32_t slot, uint3
     else nt_store2(f.gbl + (slot - kWaveCap), idx, key);
 }
 
-// Lanes with p[u] append (idx[u], key[u]) to the wave frontier and count
-// bin[u] in h.
+// Wave-private frontier entries are (index, FP32 bit pattern) pairs; the
+// descending key is formed when they are read back (desc_key).
+
+// Lanes with p[u] append (idx[u], bits[u]) to the wave frontier.  The running
+// count is wave-uniform, so each slot is that count plus the lane's rank
+// among the lanes that append.
 __device__ __forceinline__ void wappend4(const bool (&p)[4], const uint32_t (&idx)[4],
-                                         const uint32_t (&key)[4], const uint32_t (&bin)[4],
-                                         WaveFrontier& f, uint32_t* h) {
+                                         const uint32_t (&bits)[4], WaveFrontier& f) {
     uint64_t m[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) m[u] = __ballot(p[u]);
-    const uint64_t any = m[0] | m[1] | m[2] | m[3];
-    if (any == 0) return;
-    uint32_t base = f.n;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) f.n += __builtin_popcountll(m[u]);
-    if (f.n <= static_cast<uint32_t>(kWaveCap)) {  // wave-uniform: every new slot is in LDS
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (p[u]) {
-                f.lds[base + mbcnt(m[u])] = make_uint2(idx[u], key[u]);
-                lds_inc(h, bin[u]);
-            }
-            base += __builtin_popcountll(m[u]);
-        }
-        return;
-    }
+    uint32_t c[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        if (p[u]) {
-            wput(f, base + mbcnt(m[u]), idx[u], key[u]);
-            lds_inc(h, bin[u]);
-        }
-        base += __builtin_popcountll(m[u]);
+        m[u] = __ballot(p[u]);
+        c[u] = __builtin_popcountll(m[u]);
     }
+    if ((m[0] | m[1] | m[2] | m[3]) == 0) return;
+    uint32_t n = f.n;
+    const uint32_t end = n + c[0] + c[1] + c[2] + c[3];
+    if (end <= static_cast<uint32_t>(kWaveCap)) {  // wave-uniform: every new slot is in LDS
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint2* at = f.lds + n;
+            if (p[u]) at[mbcnt(m[u])] = make_uint2(idx[u], bits[u]);
+            n += c[u];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (p[u]) wput(f, n + mbcnt(m[u]), idx[u], bits[u]);
+            n += c[u];
+        }
+    }
+    f.n = end;
 }
 
 // ------------------------------------------------------------ block scans
@@ -632,39 +650,162 @@ __device__ __forceinline__ void load_chunk(const Span& sp, uint32_t base, u32x4 
     }
 }
 
+// The chunked part of a span scan: `a` holds the first chunk (loads issued);
+// later chunks are double buffered in two register sets used in turn (no
+// copies between them), the next chunk in flight while the current one is
+// processed; mid() runs as the last chunk is taken up.
+template <int U, class F, class Mid>
+__device__ __forceinline__ void chunk_loop(const Span& sp, u32x4 (&a)[U], F&& f, Mid&& mid) {
+    const uint32_t tid = threadIdx.x;
+    constexpr uint32_t C = kBlock * U;
+    if (sp.nvec == 0) {
+        mid();
+        return;
+    }
+    u32x4 b[U];
+    uint32_t base = 0;
+    while (true) {
+        // a holds the chunk at base
+        bool more = base + C < sp.nvec;
+        if (more) load_chunk<U>(sp, base + C, b);
+        else mid();
+#pragma unroll
+        for (int u = 0; u < U; ++u) f(a[u], sp.vlo + 4 * (base + u * kBlock + tid));
+        if (!more) break;
+        base += C;
+        // b holds the chunk at base
+        more = base + C < sp.nvec;
+        if (more) load_chunk<U>(sp, base + C, a);
+        else mid();
+#pragma unroll
+        for (int u = 0; u < U; ++u) f(b[u], sp.vlo + 4 * (base + u * kBlock + tid));
+        if (!more) break;
+        base += C;
+    }
+}
+
 // Calls f(bits4, index of bits4.x) over every element of the span.  issue()
 // runs first (loads whose results pre() needs, ahead of the chunk in the
 // in-order load queue), then the first chunk (U vectors per thread) and the
 // head/tail elements are loaded, then pre() runs, so their latency overlaps
-// pre().  Later chunks are double buffered: the next chunk is in flight while
-// the current one is processed.  mid() runs exactly once, as the last chunk
-// is taken up (after that chunk's loads were issued), or after the head/tail
-// elements when there is no chunk.  Every thread of the block must call it
-// with the same span.
+// pre().  Later chunks are double buffered in two register sets used in turn
+// (no copies between them): the next chunk is in flight while the current
+// one is processed.  mid() runs exactly once, as the last chunk is taken up
+// (after that chunk's loads were issued), or after the head/tail elements
+// when there is no chunk.  Every thread of the block must call it with the
+// same span.
 template <int U, class Issue, class Pre, class F, class Mid>
 __device__ __forceinline__ void scan_span(const Span& sp, Issue&& issue, Pre&& pre, F&& f, Mid&& mid) {
     const uint32_t tid = threadIdx.x;
     issue();
-    u32x4 cur[U];
-    if (sp.nvec) load_chunk<U>(sp, 0, cur);
+    u32x4 a[U];
+    if (sp.nvec) load_chunk<U>(sp, 0, a);
     const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
     uint32_t sb = kNoElem;
     if (tid < sp.nscal) sb = __float_as_uint(sp.x[se]);
     pre();
     if (sp.nscal) f(u32x4{sb, kNoElem, kNoElem, kNoElem}, se);
-    for (uint32_t base = 0; base < sp.nvec; base += kBlock * U) {
-        const bool more = base + kBlock * U < sp.nvec;
-        u32x4 nxt[U];
-        if (more) load_chunk<U>(sp, base + kBlock * U, nxt);
-        else mid();
-#pragma unroll
-        for (int u = 0; u < U; ++u) f(cur[u], sp.vlo + 4 * (base + u * kBlock + tid));
-        if (more) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        }
+    chunk_loop<U>(sp, a, f, mid);
+}
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{}):
+// a loop whose index is a compile-time constant in every step, so that arrays
+// indexed by it stay in registers however large the step is.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
     }
-    if (sp.nvec == 0) mid();
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_from<0, N>(f);
+}
+
+// Vector j of this thread's share of a span body: body vector j * kBlock + tid
+// (the filler kNoElem where it does not exist).
+__device__ __forceinline__ void load_vec(const Span& sp, uint32_t j, u32x4& v) {
+    const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo) + threadIdx.x;
+    if ((j + 1) * kBlock <= sp.nvec) {  // block-uniform: every lane has its vector
+        v = __builtin_nontemporal_load(xv + j * kBlock);
+        return;
+    }
+    if (j * kBlock + threadIdx.x < sp.nvec) v = __builtin_nontemporal_load(xv + j * kBlock);
+    else v = u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
+}
+
+// The body of a span as a rolling ring of V vector registers per thread: r[j]
+// holds (or has in flight) this thread's vector j0 + j, and each slot is
+// refilled with the vector V further on as soon as it has been processed, so
+// that about V - 1 vectors per thread stay in flight at all times (double
+// buffering in the same registers would let the count fall to zero at every
+// switch).  The caller has issued vectors 0 .. V-1.  mid() runs once, when
+// the last load has been issued.
+template <int V, class F, class Mid>
+__device__ __forceinline__ void ring_loop(const Span& sp, u32x4 (&r)[V], F&& f, Mid&& mid) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t nv = sp.nvec;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo) + tid;
+    uint32_t j0 = 0;
+    // Steady state: this round's refills are whole rows of the block.
+    while ((j0 + 2 * V) * kBlock <= nv) {
+        static_for<V>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            f(r[j], sp.vlo + 4 * ((j0 + j) * kBlock + tid));
+            r[j] = __builtin_nontemporal_load(xv + (j0 + j + V) * kBlock);
+        });
+        j0 += V;
+    }
+    // Last two rounds: refills (and vectors) may be partial or absent.
+    static_for<V>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if ((j0 + j) * kBlock < nv) f(r[j], sp.vlo + 4 * ((j0 + j) * kBlock + tid));
+        if ((j0 + j + V) * kBlock < nv) load_vec(sp, j0 + j + V, r[j]);
+    });
+    mid();
+    j0 += V;
+    static_for<V>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if ((j0 + j) * kBlock < nv) f(r[j], sp.vlo + 4 * ((j0 + j) * kBlock + tid));
+    });
+}
+
+// scan_span over a rolling ring of V vectors per thread, with the element
+// function chosen once, after pre(): fa when sel() holds, else fb (each has
+// its own loop).  The first V vectors per thread and the head/tail elements
+// are in flight while pre() runs.
+template <int V, class Issue, class Pre, class Sel, class FA, class FB, class Mid>
+__device__ __forceinline__ void scan_span2(const Span& sp, Issue&& issue, Pre&& pre, Sel&& sel,
+                                           FA&& fa, FB&& fb, Mid&& mid) {
+    const uint32_t tid = threadIdx.x;
+    issue();
+    // Nothing else is in flight here; an explicit wait lets the ring's loads
+    // issue back to back (the compiler otherwise cannot tell that no earlier
+    // load still targets the ring's registers, and waits between them).
+    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 r[V];
+    if (V * kBlock <= sp.nvec) {  // block-uniform: the whole ring exists
+        const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo) + tid;
+        static_for<V>([&](auto J) {
+            r[decltype(J)::value] = __builtin_nontemporal_load(xv + decltype(J)::value * kBlock);
+        });
+    } else {
+        static_for<V>([&](auto J) { load_vec(sp, decltype(J)::value, r[decltype(J)::value]); });
+    }
+    const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
+    uint32_t sb = kNoElem;
+    if (tid < sp.nscal) sb = __float_as_uint(sp.x[se]);
+    pre();
+    wave_priority(0);
+    if (sel()) {
+        if (sp.nscal) fa(u32x4{sb, kNoElem, kNoElem, kNoElem}, se);
+        ring_loop<V>(sp, r, fa, mid);
+    } else {
+        if (sp.nscal) fb(u32x4{sb, kNoElem, kNoElem, kNoElem}, se);
+        ring_loop<V>(sp, r, fb, mid);
+    }
+    wave_priority(1);
 }
 
 struct NoPre {
@@ -681,22 +822,37 @@ __device__ __forceinline__ void scan_span(const Span& sp, Pre&& pre, F&& f) {
     scan_span<U>(sp, NoPre{}, pre, f, NoPre{});
 }
 
-// Phase 2 admission of one 4-element group: key <= hi (and key > lo for the
-// band of Eq. 18), appended to the wave frontier with its leading digit
-// counted in h (Eq. 17).
+// Phase 2 admission of one 4-element group (Eqs. 16-17): key <= khi, and
+// key > klo for the band of Eq. 18; admitted pairs go to the wave frontier.
 template <bool BAND>
 __device__ __forceinline__ void admit4(u32x4 b, uint32_t i0, uint32_t klo, uint32_t khi,
-                                       WaveFrontier& f, uint32_t* h) {
-    uint32_t key[4], idx[4], bin[4];
+                                       WaveFrontier& f) {
+    uint32_t idx[4], bits[4];
     bool p[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        key[u] = desc_key(b[u]);
-        p[u] = key[u] <= khi && (!BAND || key[u] > klo);
+        const uint32_t key = desc_key(b[u]);
+        p[u] = key <= khi && (!BAND || key > klo);
         idx[u] = i0 + u;
-        bin[u] = key[u] >> 21;
+        bits[u] = b[u];
     }
-    wappend4(p, idx, key, bin, f, h);
+    wappend4(p, idx, bits, f);
+}
+
+// The same admission when the cutoff value is >= +0, with vt its bit pattern:
+// a non-negative pattern compared as a signed integer orders like its value
+// and every negative pattern (and the kNoElem filler) lies below, so
+// (int)bits >= (int)vt is the predicate key <= T0 in one compare.
+__device__ __forceinline__ void admit4_raw(u32x4 b, uint32_t i0, uint32_t vt, WaveFrontier& f) {
+    uint32_t idx[4], bits[4];
+    bool p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        p[u] = static_cast<int32_t>(b[u]) >= static_cast<int32_t>(vt);
+        idx[u] = i0 + u;
+        bits[u] = b[u];
+    }
+    wappend4(p, idx, bits, f);
 }
 
 // ------------------------------------------------------------ row pieces
@@ -724,20 +880,29 @@ struct Cuts {
     uint32_t t0, t1;
 };
 
+// Counts a batch of view samples (kNoElem: none) in the coarse histogram h.
+__device__ __forceinline__ void view_count(const uint32_t (&b)[kSampleVec], uint32_t* h) {
+#pragma unroll
+    for (int u = 0; u < kSampleVec; ++u)
+        if (b[u] != kNoElem) lds_inc(h, coarse_of_bits(b[u]));
+}
+
 // Phase 1: coarse histogram of the view into h (cleared and visible; `first`
-// is the first batch of samples when it was loaded ahead), tau0 and tau1
-// (Eq. 15), and their inclusive FP32 cutoffs from the compile-time table.
-// All sample loads of a batch are issued before any is used.  Ends with a
-// barrier.
+// is the first batch of samples when it was loaded ahead, else samples
+// [0, counted) are already in h), tau0 and tau1 (Eq. 15), and their
+// inclusive FP32 cutoffs from the compile-time table.  All sample loads of a
+// batch are issued before any is used.  Ends with a barrier.
 __device__ __forceinline__ Cuts phase1(const float* x, uint32_t a, uint32_t nv, int s, uint32_t q, uint32_t q1,
-                       uint32_t* h, Shared& sm, const uint32_t* first = nullptr) {
+                       uint32_t* h, Shared& sm, const uint32_t* first = nullptr,
+                       uint32_t counted = 0) {
     const uint32_t tid = threadIdx.x;
     if (first) {
 #pragma unroll
         for (int u = 0; u < kSampleVec; ++u)
             if (first[u] != kNoElem) lds_inc(h, coarse_of_bits(first[u]));
+        counted = kBlock * kSampleVec;
     }
-    for (uint32_t j0 = first ? kBlock * kSampleVec : 0u; j0 < nv; j0 += kBlock * kSampleVec) {
+    for (uint32_t j0 = counted; j0 < nv; j0 += kBlock * kSampleVec) {
         uint32_t b[kSampleVec];
 #pragma unroll
         for (int u = 0; u < kSampleVec; ++u) {
@@ -768,16 +933,15 @@ __device__ __forceinline__ uint32_t publish_waves(const WaveFrontier& wf, Shared
 // Exact coarse route (Sec. 4.3, Eq. 20) over [0, L): coarse histogram of
 // every value, tau* = min{b : C(b) >= K}, then one classification pass (from
 // registers when the row fits one chunk, else a second read) that
-// commits c < tau* to the output and retains c == tau* in the wave frontier
-// with its leading-digit histogram in h0.  Returns k0 = K - |E0|; the
-// committed count is left in sm.out_cnt and the frontier sizes in sm.wcnt.
+// commits c < tau* to the output and retains c == tau* in the wave frontier.
+// Returns k0 = K - |E0|; the committed count is left in sm.out_cnt and the
+// frontier sizes in sm.wcnt.  hc: a 2048-bin LDS histogram (any contents).
 template <bool REGS>
 __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint32_t k,
                                                 int32_t* outp, WaveFrontier& wf, uint32_t* hc,
-                                                uint32_t* h0, Shared& sm) {
+                                                Shared& sm) {
     __syncthreads();  // earlier readers of the frontier and histograms are done
     clear_hist(hc);
-    clear_hist(h0);
     if (threadIdx.x == 0) sm.out_cnt = 0;
     wf.n = 0;
     __syncthreads();
@@ -790,7 +954,7 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
     uint32_t tau = 0;
     auto classify = [&](u32x4 b, uint32_t i0) {
         bool com[4], ret[4];
-        uint32_t idx[4], key[4], bin[4];
+        uint32_t idx[4], bits[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const bool valid = b[u] != kNoElem;
@@ -798,11 +962,10 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
             com[u] = valid && cc < tau;
             ret[u] = valid && cc == tau;
             idx[u] = i0 + u;
-            key[u] = desc_key(b[u]);
-            bin[u] = key[u] >> 21;
+            bits[u] = b[u];
         }
         commit4(com, idx, outp, k, sm);
-        wappend4(ret, idx, key, bin, wf, h0);
+        wappend4(ret, idx, bits, wf);
     };
     const uint32_t t[1] = {k};
     if (REGS && sp.nvec <= static_cast<uint32_t>(kBlock * kRowVec)) {
@@ -839,76 +1002,76 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
 }
 
 // Phase 3 (Sec. 4.4) with the whole frontier in registers: each thread holds
-// up to R (index, key) entries given by load(u, idx, key).  With BUILD_H0 the
-// leading-digit histogram is counted here into hc (cleared and visible);
-// otherwise hc already holds it.  kq is the remaining quota and out_base the
-// number of indices committed before.  Each round finds b_j (Eq. 23),
-// commits the lower digit groups (Eq. 24) and keeps the boundary group
-// (Eq. 25) while counting its next digit; output slots come from block
-// prefix sums and are staged in LDS (the frontier buffer is free once the
-// entries are in registers), then written out with coalesced stores.  After
-// the last digit the boundary group holds equal keys and its first `need`
-// entries fill the output.  Writes out[out_base, k).
-template <int R, bool BUILD_H0, class Load>
-__device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t* hn, uint32_t kq,
+// up to R (index, key) entries given by load(u, idx, key); kq is the
+// remaining quota and out_base the number of indices committed before.  A
+// radix selection over the descending FP32 key whose digit window follows
+// the frontier: the active keys lie in [lo, hi] (at first the frontier's
+// smallest and largest key), a round's digit is (key - lo) >> sh with sh the
+// smallest shift that maps [lo, hi] into the 2048 bins, b = min{b : H(b) >=
+// kq} (Eq. 23), the lower bins are committed (Eq. 24) and bin b is kept with
+// [lo, hi] narrowed to it (Eq. 25).  Over the whole 32-bit key range the
+// rounds are the 11 + 11 + 10 digits; over the narrow range that a frontier
+// of candidates spans, one round usually leaves a boundary group of a few
+// entries.  A boundary group of at most 64 entries is finished by one wave
+// (rank by full key); after a round with sh == 0 the boundary group holds
+// equal keys and its first `need` entries fill the output.  Output slots come
+// from block prefix sums and are staged in LDS (the frontier buffer is free
+// once the entries are in registers), then written out with coalesced
+// stores.  hA, hB: two 2048-bin LDS histograms (any contents).  Writes
+// out[out_base, k).
+template <int R, class Load>
+__device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hA, uint32_t* hB, uint32_t kq,
                                             uint32_t out_base, int32_t* outp, uint32_t k,
                                             Shared& sm) {
     uint32_t idx[R], key[R];
     uint32_t act = 0;
+    uint32_t mn = kNoElem, mx = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) {
         idx[u] = 0;
         key[u] = kNoElem;
-        if (load(u, idx[u], key[u])) act |= 1u << u;
-    }
-    if (BUILD_H0) {
-        // The leading digits of a candidate tail crowd into a few bins next
-        // to the cutoff's, where 64 lanes adding to one LDS word serialize.
-        // Entries in the wave's four highest leading-digit bins (the values
-        // nearest the cutoff) are counted in registers and added once per
-        // wave; the rest (the spread-out larger values) count themselves.
-        uint32_t dmax = 0;
-#pragma unroll
-        for (int u = 0; u < R; ++u)
-            if ((act >> u) & 1u) dmax = (key[u] >> 21) > dmax ? (key[u] >> 21) : dmax;
-        dmax = wave_max(dmax);
-        uint32_t c[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-            if ((act >> u) & 1u) {
-                const uint32_t off = dmax - (key[u] >> 21);
-                if (off < 4) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) c[i] += off == static_cast<uint32_t>(i) ? 1u : 0u;
-                } else {
-                    lds_inc(hc, key[u] >> 21);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t tot = readlane(wave_incl_scan(c[i]), 63);
-            if (lane() == 0 && tot && dmax >= static_cast<uint32_t>(i)) lds_add(hc, dmax - i, tot);
+        if (load(u, idx[u], key[u])) {
+            act |= 1u << u;
+            mn = key[u] < mn ? key[u] : mn;
+            mx = key[u] > mx ? key[u] : mx;
         }
     }
-    if (threadIdx.x == 0) sm.small_n = 0;
+    if (threadIdx.x == 0) {
+        sm.small_n = 0;
+        sm.kext[0] = kNoElem;
+        sm.kext[1] = 0;
+    }
+    clear_hist(hA);
     __syncthreads();  // entries are in registers; the frontier buffer becomes the stage
+    lds_extremes(&sm.kext[0], mn, mx);
+    __syncthreads();
+    uint32_t lo = readfirst(sm.kext[0]);
+    uint32_t hi = readfirst(sm.kext[1]);
     uint32_t* stage = reinterpret_cast<uint32_t*>(sm.front);
     const uint32_t base0 = out_base;
-#pragma unroll
+    // Each round at least halves the window's bit length in the worst case
+    // (32 -> 21 -> 10 -> 0 bits beyond the digit), so the third round has
+    // sh == 0 and is the last.
     for (int j = 0; j < 3; ++j) {
-        if (j < 2) clear_hist(hn);
+        const uint32_t span = hi - lo;
+        const uint32_t bl = span ? 32u - static_cast<uint32_t>(__builtin_clz(span)) : 0u;
+        const uint32_t sh = bl > 11 ? bl - 11 : 0u;
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+            if ((act >> u) & 1u) lds_inc(hA, (key[u] - lo) >> sh);
+        clear_hist(hB);  // the next round's histogram, or the boundary list
+        __syncthreads();
         const uint32_t t[1] = {kq};
-        block_find<1>(hc, t, sm);
+        block_find<1>(hA, t, sm);
         const uint32_t b = sm.res[0], before = sm.res[1];
-        const uint32_t inb = hc[b];
+        const uint32_t inb = hA[b];
         const bool exact_fill = before + inb == kq;  // the boundary group fits exactly
-        const bool last = exact_fill || j == 2;
+        const bool last = exact_fill || sh == 0;
         const uint32_t need = kq - before;
         uint32_t com = 0, tie = 0, keep = 0;
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            const uint32_t d = digit(j, key[u]);
+            const uint32_t d = (key[u] - lo) >> sh;
             const bool on = (act >> u) & 1u;
             if (on && (d < b || (exact_fill && d == b))) com |= 1u << u;
             if (on && !exact_fill && d == b) {
@@ -939,11 +1102,11 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
         if (last) break;
         if (inb <= 64) {
             // A boundary group of at most 64 entries is finished by one wave:
-            // gathered into a list (in hn, free from here on), each entry's
-            // rank among the group by full key (equal keys by list position)
-            // is its order, and the `need` first take the remaining slots.
-            // The same selection the remaining digit rounds would make.
-            uint2* list = reinterpret_cast<uint2*>(hn);
+            // gathered into a list (in hB), each entry's rank among the group
+            // by full key (equal keys by list position) is its order, and the
+            // `need` first take the remaining slots.  The same selection the
+            // remaining rounds would make.
+            uint2* list = reinterpret_cast<uint2*>(hB);
 #pragma unroll
             for (int u = 0; u < R; ++u) {
                 const bool kp = (keep >> u) & 1u;
@@ -966,14 +1129,13 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hc, uint32_t*
             }
             break;
         }
-#pragma unroll
-        for (int u = 0; u < R; ++u)
-            if ((keep >> u) & 1u) lds_inc(hn, digit(j + 1, key[u]));
         act = keep;
         out_base += tot_c;
         kq = need;
-        __syncthreads();
-        uint32_t* th = hc; hc = hn; hn = th;
+        lo += b << sh;
+        const uint64_t top = static_cast<uint64_t>(lo) + ((1ull << sh) - 1ull);
+        if (top < hi) hi = static_cast<uint32_t>(top);
+        uint32_t* th = hA; hA = hB; hB = th;
     }
     __syncthreads();
     for (uint32_t j = base0 + threadIdx.x; j < k; j += kBlock) outp[j] = static_cast<int32_t>(stage[j]);
@@ -1066,10 +1228,12 @@ __device__ __forceinline__ void refine(Frontier cur, Frontier nxt, uint32_t* hc,
 }
 
 // Copies the wave frontiers (LDS share, then spill range) into one
-// contiguous frontier dst and returns whether all of its keys are equal
+// contiguous frontier dst, counts the leading digit of every key in h (any
+// contents on entry) and returns whether all of its keys are equal
 // (block-uniform; ends with a barrier).
 __device__ __forceinline__ bool compact_waves(const uint2* spill_base, int64_t spill_len,
-                                              uint2* dst, Shared& sm) {
+                                              uint2* dst, uint32_t* h, Shared& sm) {
+    clear_hist(h);
     if (threadIdx.x == 0) {
         uint32_t o = 0;
         for (int w = 0; w < kWaves; ++w) { sm.offs[0][w] = o; o += sm.wcnt[w]; }
@@ -1091,7 +1255,9 @@ __device__ __forceinline__ bool compact_waves(const uint2* spill_base, int64_t s
             const u32x2 t = nt_load2(spill_base + w * spill_len + (e - kWaveCap));
             v = make_uint2(t.x, t.y);
         }
+        v.y = desc_key(v.y);
         nt_store2(dst + g, v.x, v.y);
+        hist_add(h, v.y >> 21, true, __ballot(true));
         mn = v.y < mn ? v.y : mn;
         mx = v.y > mx ? v.y : mx;
     }
@@ -1101,11 +1267,12 @@ __device__ __forceinline__ bool compact_waves(const uint2* spill_base, int64_t s
 }
 
 // Phase 3 for a wave-private frontier of C entries (sizes in sm.wcnt, visible),
-// leading-digit histogram h1, quota kq, sm.out_cnt indices already committed.
-// When every wave's share fits on chip the frontier is refined from
-// registers; otherwise it is gathered into `contig` and refined through
-// ping-pong buffers (LDS, then `spare`).  spill_base/spill_len locate the
-// wave spills; `spare` may overlap them.
+// quota kq, sm.out_cnt indices already committed; h1, h0: two 2048-bin LDS
+// histograms (any contents).  When every wave's share fits on chip the
+// frontier is refined from registers; otherwise it is gathered into `contig`
+// (counting the leading digit) and refined through ping-pong buffers (LDS,
+// then `spare`).  spill_base/spill_len locate the wave spills; `spare` may
+// overlap them.
 __device__ __forceinline__ void finish_waves(uint32_t C, const uint2* spill_base,
                                              int64_t spill_len, uint2* contig, uint2* spare,
                                              uint32_t* h1, uint32_t* h0, uint32_t kq,
@@ -1117,19 +1284,19 @@ __device__ __forceinline__ void finish_waves(uint32_t C, const uint2* spill_base
     if (wmax <= static_cast<uint32_t>(kWaveCap)) {
         const uint32_t mine = sm.wcnt[wave()];
         const uint2* reg = sm.front + wave() * kWaveCap;
-        refine_regs<kWaveRegs, false>(
+        refine_regs<kWaveRegs>(
             [&](int u, uint32_t& i, uint32_t& key) {
                 const uint32_t e = lane() + 64 * u;
                 if (e >= mine) return false;
                 const uint2 v = reg[e];
                 i = v.x;
-                key = v.y;
+                key = desc_key(v.y);
                 return true;
             },
             h1, h0, kq, out_base, outp, k, sm);
         return;
     }
-    if (compact_waves(spill_base, spill_len, contig, sm)) {
+    if (compact_waves(spill_base, spill_len, contig, h1, sm)) {
         // Every entry carries the same key (a constant row, say): no value
         // outside the frontier ranks above it, so its first kq entries are
         // the rest of the answer.
@@ -1178,12 +1345,12 @@ __device__ __forceinline__ int publish_ticket(const Params& p, uint32_t t, int m
 
 // One row, whole-row ownership (persistent mapping).  L is the row's valid
 // length; `looked`: vb holds the row's first batch of view samples, loaded
-// at the end of the previous row.  Thread 0 holds ticket t, drawn when the
+// when the previous row was done.  Thread 0 holds ticket t, drawn when the
 // row started.  sliceA holds the wave spills, sliceB is the contiguous
 // frontier of the general path.  On the sampled route the next row is
-// published at the end of Phase 1, its length is read while this row streams, and
-// its first batch of view samples is loaded when this row is done; nr.row <
-// 0 means the next row is not known yet.
+// published at the end of Phase 1, its length is read while this row
+// streams, and its first batch of view samples is loaded when this row is
+// done; nr.row < 0 means the next row is not known yet.
 template <int S, bool DUAL, bool HINT>
 __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t L, bool looked,
                                               const uint32_t (&vb)[kSampleVec], uint32_t t,
@@ -1221,19 +1388,27 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
             uint32_t T0 = 0, T1 = 0;
             int32_t ke_next = 0;
             bool on = false;
+            // h0 is clear (every row leaves it so).  Samples loaded ahead have
+            // long arrived: they are counted before the row's first loads are
+            // issued, so that counting them waits for nothing else.
+            if (!hinted && looked) view_count(vb, h0);
+            uint32_t vfirst[kSampleVec];
             const Span sp = make_span(x, 0, L);
-            scan_span<kRowVec>(
+            scan_span2<kScanVec>(
                 sp,
                 [&]() {
-                    clear_hist(h1);
-                    clear_hist(h0);
+                    if (!hinted && !looked) view_batch(x, a, nv, S, 0u, vfirst);
+                },
+                [&]() {
                     if (threadIdx.x == 0) sm.out_cnt = 0;
-                    __syncthreads();
                     if (hinted) {
                         T0 = hkey;  // the proposal replaces Phase 1; no band
                         T1 = hkey;
+                        __syncthreads();
                     } else {
-                        const Cuts c = phase1(x, a, nv, S, q, q1, h0, sm, looked ? vb : nullptr);
+                        if (!looked) view_count(vfirst, h0);
+                        const Cuts c = phase1(x, a, nv, S, q, q1, h0, sm, nullptr,
+                                              static_cast<uint32_t>(kBlock * kSampleVec));
                         T0 = c.t0;
                         T1 = c.t1;
                     }
@@ -1244,7 +1419,10 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                     nr.row = sm.next_row;
                     if (nr.row < m_live) ke_next = p.ke[nr.row];
                 },
-                [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, wf, h1); },
+                // a cutoff value >= +0 (T0 <= 0x7FFFFFFF) takes the raw compare
+                [&]() { return T0 <= 0x7FFFFFFFu; },
+                [&](u32x4 b, uint32_t i0) { admit4_raw(b, i0, T0 ^ 0x7FFFFFFFu, wf); },
+                [&](u32x4 b, uint32_t i0) { admit4<false>(b, i0, 0u, T0, wf); },
                 [&]() {
                     // The next row's geometry (its length has arrived by now).
                     nr.L = nr.row < m_live ? clamp_len(ke_next, p.n) : 0u;
@@ -1261,7 +1439,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                 route = TOPKF_ROUTE_EXACT_UNDERFILL;
                 if (DUAL && T1 > T0) {
                     scan_span<kRowVec>(sp, NoPre{}, [&](u32x4 b, uint32_t i0) {
-                        admit4<true>(b, i0, T0, T1, wf, h1);
+                        admit4<true>(b, i0, T0, T1, wf);
                     });
                     __syncthreads();
                     C = publish_waves(wf, sm);
@@ -1275,7 +1453,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     uint32_t kq = k;
     if (!certified) {
         // The no-view plan serves short rows: keep them in registers.
-        kq = exact_route<S == 0>(x, L, k, outp, wf, h0, h1, sm);
+        kq = exact_route<S == 0>(x, L, k, outp, wf, h0, sm);
         C = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) C += sm.wcnt[w];
@@ -1286,9 +1464,10 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     for (int w = 0; w < kWaves; ++w) spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
     if (spill) count_route(p, TOPKF_ROUTE_SPILL);
     finish_waves(C, sliceA, wsl, sliceB, sliceA, h1, h0, kq, outp, k, sm);
-    // The next row's first batch of view samples goes out now, so that its
-    // Phase 1 overlaps the loads of its first chunk and the sampled lines are
-    // still cached when its scan reads them.
+    clear_hist(h0);  // for the next row's view (made visible by the caller's barrier)
+    // The next row's first batch of view samples goes out now, so that it has
+    // arrived when that row starts, and the sampled lines are still cached
+    // when its scan reads them.
     if constexpr (S > 0) {
         if (nr.looked) view_batch(xn, na, nnv, S, 0u, nr.vb);
     }
@@ -1312,6 +1491,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     uint32_t vb[kSampleVec];
 #pragma unroll
     for (int u = 0; u < kSampleVec; ++u) vb[u] = kNoElem;
+    wave_priority(1);
+    clear_hist(sm.hist[0]);  // the first row's view histogram
+    __syncthreads();
     while (row < m_live) {
         uint32_t t = 0;
         if (threadIdx.x == 0) t = atomicAdd(p.counters, 1u);
@@ -1405,7 +1587,7 @@ __device__ __forceinline__ void kv_exact_row(const Params& p, const RowGeom& g, 
     uint2* region2 = region + slice_len(p.n);
     const int64_t wsl = wave_spill_len(p.n);
     WaveFrontier wf{sm.front + wave() * kWaveCap, region + wave() * wsl, 0};
-    const uint32_t kq = exact_route<true>(x, g.L, k, outp, wf, sm.hist[0], sm.hist[1], sm);
+    const uint32_t kq = exact_route<true>(x, g.L, k, outp, wf, sm.hist[0], sm);
     uint32_t C = 0;
     bool spill = false;
 #pragma unroll
@@ -1716,7 +1898,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 live[u] = gi < ctot;
             }
         }
-        refine_regs<kRegs, true>(
+        refine_regs<kRegs>(
             [&](int u, uint32_t& i, uint32_t& key) {
                 if (!live[u]) return false;
                 const uint2 t2 = region[src[u]];
@@ -2053,7 +2235,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     uint2* region = kv_region(p, row);
     uint2* region2 = region + slice_len(p.n);
     if (nq <= static_cast<uint32_t>(kBlock * kRegs)) {
-        refine_regs<kRegs, true>(
+        refine_regs<kRegs>(
             [&](int u, uint32_t& i, uint32_t& key) {
                 const uint32_t gi = threadIdx.x + kBlock * u;
                 if (gi >= nq) return false;
