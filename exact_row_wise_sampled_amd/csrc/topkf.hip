@@ -2396,12 +2396,13 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         r.family = TOPKF_FAMILY_PERSISTENT;
         r.workers = static_cast<int32_t>(m_cap < pool ? rows : pool);
         r.splits = 1;
-        // A worker that recovers an underfilled row holds up the end of the
-        // launch; on causal prefill K~ = 1.75K underfills about 0.3 % of rows
-        // against 1.5 % for the 1.5K of Sec. 4.2, at 16 % more candidates
-        // (measured 3.6 % faster).
-        // KV-split keeps 1.5K: its parts collect the band in the same pass.
-        r.primary_quarters = 7;
+        // A worker that recovers an underfilled row re-reads it and holds up
+        // the end of the launch.  On causal prefill (measured): K~ = 1.5K
+        // (Sec. 4.2) rescues 2 % of rows with the band, 1.75K 0.2 %, 2K none
+        // (Eq. 8 bound 0.02 %) at 30 % more candidates than 1.5K; the
+        // candidates cost little since a row's refinement is one histogram
+        // round, and 2K is 4 % faster than 1.75K (2.25K no faster).
+        r.primary_quarters = 8;
     } else {
         // Parts per row: enough to fill the pool, but no segment shorter
         // than 16K columns (shorter segments lose more to the replicated

@@ -81,7 +81,7 @@ def test_planner_maps_workload_shapes():
             assert pl.workers == min(m, 2 * cus)
     assert long_.splits == 32 and decode.splits == 8
     assert decode.dual == 0 and decode.primary_quarters == 8
-    assert prefill.primary_quarters == 7 and prefill.band_quarters == 10
+    assert prefill.primary_quarters == 8 and prefill.band_quarters == 10
 
 
 def test_planner_is_deterministic_and_validates():
