@@ -634,19 +634,28 @@ __device__ __forceinline__ Span make_span(const float* x, uint32_t lo, uint32_t 
     return s;
 }
 
+// Body vector vi of a span, or the filler kNoElem when vi is past its end.
+__device__ __forceinline__ u32x4 in_span(const u32x4& v, uint32_t vi, uint32_t nvec) {
+    return vi < nvec ? v : u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
+}
+
+// Loads this thread's vectors base + u * kBlock + tid (u < U) of the span
+// body.  In a partial chunk, lanes past the end load the body's last vector
+// instead (every load in bounds and unconditional, so that the loads issue
+// back to back: a filler written into a load's destination first makes the
+// compiler wait on earlier loads); consumers apply in_span.  nvec >= 1.
 template <int U>
 __device__ __forceinline__ void load_chunk(const Span& sp, uint32_t base, u32x4 (&v)[U]) {
-    const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo) + base + threadIdx.x;
+    const u32x4* xb = reinterpret_cast<const u32x4*>(sp.x + sp.vlo);
     if (base + U * kBlock <= sp.nvec) {  // a whole chunk inside the span: no per-lane bounds
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(xv + u * kBlock);
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(xb + base + u * kBlock + threadIdx.x);
         return;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const uint32_t vi = base + u * kBlock + threadIdx.x;
-        if (vi < sp.nvec) v[u] = __builtin_nontemporal_load(xv + u * kBlock);
-        else v[u] = u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
+        v[u] = __builtin_nontemporal_load(xb + (vi < sp.nvec ? vi : sp.nvec - 1));
     }
 }
 
@@ -670,7 +679,10 @@ __device__ __forceinline__ void chunk_loop(const Span& sp, u32x4 (&a)[U], F&& f,
         if (more) load_chunk<U>(sp, base + C, b);
         else mid();
 #pragma unroll
-        for (int u = 0; u < U; ++u) f(a[u], sp.vlo + 4 * (base + u * kBlock + tid));
+        for (int u = 0; u < U; ++u) {
+            const uint32_t vi = base + u * kBlock + tid;
+            f(in_span(a[u], vi, sp.nvec), sp.vlo + 4 * vi);
+        }
         if (!more) break;
         base += C;
         // b holds the chunk at base
@@ -678,7 +690,10 @@ __device__ __forceinline__ void chunk_loop(const Span& sp, u32x4 (&a)[U], F&& f,
         if (more) load_chunk<U>(sp, base + C, a);
         else mid();
 #pragma unroll
-        for (int u = 0; u < U; ++u) f(b[u], sp.vlo + 4 * (base + u * kBlock + tid));
+        for (int u = 0; u < U; ++u) {
+            const uint32_t vi = base + u * kBlock + tid;
+            f(in_span(b[u], vi, sp.nvec), sp.vlo + 4 * vi);
+        }
         if (!more) break;
         base += C;
     }
@@ -724,15 +739,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Vector j of this thread's share of a span body: body vector j * kBlock + tid
-// (the filler kNoElem where it does not exist).
+// (as load_chunk: lanes past the end load the body's last vector; consumers
+// apply in_span).  nvec >= 1.
 __device__ __forceinline__ void load_vec(const Span& sp, uint32_t j, u32x4& v) {
-    const u32x4* xv = reinterpret_cast<const u32x4*>(sp.x + sp.vlo) + threadIdx.x;
-    if ((j + 1) * kBlock <= sp.nvec) {  // block-uniform: every lane has its vector
-        v = __builtin_nontemporal_load(xv + j * kBlock);
-        return;
-    }
-    if (j * kBlock + threadIdx.x < sp.nvec) v = __builtin_nontemporal_load(xv + j * kBlock);
-    else v = u32x4{kNoElem, kNoElem, kNoElem, kNoElem};
+    const u32x4* xb = reinterpret_cast<const u32x4*>(sp.x + sp.vlo);
+    const uint32_t vi = j * kBlock + threadIdx.x;
+    v = __builtin_nontemporal_load(xb + (vi < sp.nvec ? vi : sp.nvec - 1));
 }
 
 // The body of a span as a rolling ring of V vector registers per thread: r[j]
@@ -760,14 +772,16 @@ __device__ __forceinline__ void ring_loop(const Span& sp, u32x4 (&r)[V], F&& f, 
     // Last two rounds: refills (and vectors) may be partial or absent.
     static_for<V>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        if ((j0 + j) * kBlock < nv) f(r[j], sp.vlo + 4 * ((j0 + j) * kBlock + tid));
+        const uint32_t vi = (j0 + j) * kBlock + tid;
+        if ((j0 + j) * kBlock < nv) f(in_span(r[j], vi, nv), sp.vlo + 4 * vi);
         if ((j0 + j + V) * kBlock < nv) load_vec(sp, j0 + j + V, r[j]);
     });
     mid();
     j0 += V;
     static_for<V>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        if ((j0 + j) * kBlock < nv) f(r[j], sp.vlo + 4 * ((j0 + j) * kBlock + tid));
+        const uint32_t vi = (j0 + j) * kBlock + tid;
+        if ((j0 + j) * kBlock < nv) f(in_span(r[j], vi, nv), sp.vlo + 4 * vi);
     });
 }
 
@@ -790,8 +804,10 @@ __device__ __forceinline__ void scan_span2(const Span& sp, Issue&& issue, Pre&& 
         static_for<V>([&](auto J) {
             r[decltype(J)::value] = __builtin_nontemporal_load(xv + decltype(J)::value * kBlock);
         });
-    } else {
-        static_for<V>([&](auto J) { load_vec(sp, decltype(J)::value, r[decltype(J)::value]); });
+    } else if (sp.nvec) {
+        static_for<V>([&](auto J) {
+            if (decltype(J)::value * kBlock < sp.nvec) load_vec(sp, decltype(J)::value, r[decltype(J)::value]);
+        });
     }
     const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
     uint32_t sb = kNoElem;
@@ -979,6 +995,8 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
         const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
         const u32x4 sb{tid < sp.nscal ? __float_as_uint(sp.x[se]) : kNoElem, kNoElem, kNoElem, kNoElem};
         count(sb, se);
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u) v[u] = in_span(v[u], u * kBlock + tid, sp.nvec);
 #pragma unroll
         for (int u = 0; u < kRowVec; ++u) count(v[u], 0u);
         __syncthreads();
@@ -1638,8 +1656,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     uint2* region = kv_region(p, row);
     uint32_t* h0 = sm.hist[0];
 
-    // Phases 1 and 2 for this part; the segment's first chunk is in flight
-    // while the (replicated) view is histogrammed.
+    // Phases 1 and 2 for this part.  The view samples are loaded first and
+    // awaited before the segment's loads go out: issued together, the
+    // samples queue behind every part's segment loads in the memory system
+    // and Phase 1 waits for the whole flood (measured on decode: samples
+    // complete 6 us after launch).  The segment's first chunk is then in
+    // flight while the (replicated) view is histogrammed.
     uint32_t T0 = 0, T1 = 0;
     // Candidates are staged in the wave's share of the LDS frontier with
     // wave-uniform counts (primary from the bottom, band from the top) and
@@ -1651,10 +1673,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     bool wspill = false;
     uint32_t vb[kSampleVec];
     const Span sp = make_span(x, lo, hi);
+    bool raw = false;  // the cutoff value is >= +0: admission by raw compare (admit4_raw)
+    uint32_t vt0 = 0;
     scan_span<kSegVec>(
         sp,
         [&]() {
-            if (!hinted) view_batch(x, g.a, g.nv, S, 0u, vb);
+            if (!hinted) {
+                view_batch(x, g.a, g.nv, S, 0u, vb);
+                __builtin_amdgcn_s_waitcnt(0);
+            }
         },
         [&]() {
             clear_hist(h0);
@@ -1674,21 +1701,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 T0 = c.t0;
                 T1 = c.t1;
             }
+            raw = !DUAL && T0 <= 0x7FFFFFFFu;
+            vt0 = T0 ^ 0x7FFFFFFFu;
         },
         [&](u32x4 b, uint32_t i0) {
             uint32_t key[4];
             bool pp[4], pb[4];
             uint64_t mp[4], mb[4];
             uint32_t tp = 0, tb = 0;
+            if (raw) {
+                // the signed compare of admit4_raw; admitted values are >= +0
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                key[u] = desc_key(b[u]);
-                pp[u] = key[u] <= T0;
-                pb[u] = DUAL && key[u] > T0 && key[u] <= T1;
-                mp[u] = __builtin_amdgcn_ballot_w64(pp[u]);
-                mb[u] = DUAL ? __builtin_amdgcn_ballot_w64(pb[u]) : 0ull;
-                tp += __builtin_popcountll(mp[u]);
-                tb += __builtin_popcountll(mb[u]);
+                for (int u = 0; u < 4; ++u) {
+                    pp[u] = static_cast<int32_t>(b[u]) >= static_cast<int32_t>(vt0);
+                    key[u] = b[u] ^ 0x7FFFFFFFu;
+                    pb[u] = false;
+                    mp[u] = __builtin_amdgcn_ballot_w64(pp[u]);
+                    mb[u] = 0ull;
+                    tp += __builtin_popcountll(mp[u]);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    key[u] = desc_key(b[u]);
+                    pp[u] = key[u] <= T0;
+                    pb[u] = DUAL && key[u] > T0 && key[u] <= T1;
+                    mp[u] = __builtin_amdgcn_ballot_w64(pp[u]);
+                    mb[u] = DUAL ? __builtin_amdgcn_ballot_w64(pb[u]) : 0ull;
+                    tp += __builtin_popcountll(mp[u]);
+                    tb += __builtin_popcountll(mb[u]);
+                }
             }
             if (sp_n + sb_n + tp + tb <= static_cast<uint32_t>(kWaveCap)) {
                 // Staged in the wave's LDS share: primary upward, band downward.
