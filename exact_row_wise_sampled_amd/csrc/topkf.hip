@@ -106,6 +106,8 @@ struct alignas(16) Shared {
     uint32_t kext[2];  // smallest and largest key of a large frontier
     uint32_t small_n;  // register refinement: entries in the small boundary list
     uint32_t spilled;  // KV-split scan: some wave wrote candidates past its stage
+    uint32_t fkey[2];  // KV-split scan: the part's flood key per kind (kNoElem: none yet)
+    uint32_t fcnt[2];  // KV-split scan: copies of it in bulk batches so far
     alignas(16) uint32_t hist[2][kBins];
     uint2 front[kFront];
 };
@@ -721,6 +723,35 @@ __device__ __forceinline__ void scan_span(const Span& sp, Issue&& issue, Pre&& p
     pre();
     if (sp.nscal) f(u32x4{sb, kNoElem, kNoElem, kNoElem}, se);
     chunk_loop<U>(sp, a, f, mid);
+}
+
+// scan_span with the element step chosen after pre(): sel() returns 0, 1 or
+// 2 and the body is scanned with f0, f1 or f2 (one chunk loop compiled per
+// step, so a scan runs only the code of its own step).  Only the last N
+// steps are compiled (N = 2: sel() never returns 0; N = 1: always f1).
+template <int U, int N, class Issue, class Pre, class Sel, class F0, class F1, class F2, class Mid>
+__device__ __forceinline__ void scan_span_sel(const Span& sp, Issue&& issue, Pre&& pre, Sel&& sel,
+                                              F0&& f0, F1&& f1, F2&& f2, Mid&& mid) {
+    const uint32_t tid = threadIdx.x;
+    issue();
+    u32x4 a[U];
+    if (sp.nvec) load_chunk<U>(sp, 0, a);
+    const uint32_t se = tid < sp.head ? sp.lo + tid : sp.tlo + (tid - sp.head);
+    uint32_t sb = kNoElem;
+    if (tid < sp.nscal) sb = __float_as_uint(sp.x[se]);
+    pre();
+    const int which = sel();
+    const u32x4 s4{sb, kNoElem, kNoElem, kNoElem};
+    if (N > 2 && which == 0) {
+        if (sp.nscal) f0(s4, se);
+        chunk_loop<U>(sp, a, f0, mid);
+    } else if (N < 2 || which == 1) {
+        if (sp.nscal) f1(s4, se);
+        chunk_loop<U>(sp, a, f1, mid);
+    } else {
+        if (sp.nscal) f2(s4, se);
+        chunk_loop<U>(sp, a, f2, mid);
+    }
 }
 
 // f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{}):
@@ -1673,64 +1704,38 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     bool wspill = false;
     uint32_t vb[kSampleVec];
     const Span sp = make_span(x, lo, hi);
-    bool raw = false;  // the cutoff value is >= +0: admission by raw compare (admit4_raw)
-    uint32_t vt0 = 0;
-    scan_span<kSegVec>(
-        sp,
-        [&]() {
-            if (!hinted) {
-                view_batch(x, g.a, g.nv, S, 0u, vb);
-                __builtin_amdgcn_s_waitcnt(0);
-            }
-        },
-        [&]() {
-            clear_hist(h0);
-            if (threadIdx.x == 0) {
-                sm.cnt[0] = 0;
-                sm.cnt[1] = 0;
-                sm.kext[0] = kNoElem;
-                sm.kext[1] = 0;
-                sm.spilled = 0;
-            }
-            __syncthreads();
-            if (hinted) {
-                T0 = hkey;  // the proposal replaces Phase 1; no band
-                T1 = hkey;
-            } else {
-                const Cuts c = phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
-                T0 = c.t0;
-                T1 = c.t1;
-            }
-            raw = !DUAL && T0 <= 0x7FFFFFFFu;
-            vt0 = T0 ^ 0x7FFFFFFFu;
-        },
-        [&](u32x4 b, uint32_t i0) {
+    uint32_t vt0 = 0;         // raw admission: signed-int form of the cutoff
+    int mode = 0;             // 0: raw compare, 1: key compare, 2: key compare with flood control
+    uint32_t full[2] = {kNoElem, kNoElem};
+    // The element step, in three compiled forms so that each part runs a
+    // straight-line scan with only the code its mode needs.  RAW: the cutoff
+    // value is >= +0 and admission is the signed compare of admit4_raw.
+    // FLOOD: the view put many times the target sample count at or above the
+    // cutoff (a constant or heavily tied row); a wave whose stage is full then
+    // also tracks a flood key per part and kind (below).
+    auto step = [&](auto raw_c, auto flood_c) {
+        constexpr bool RAW = decltype(raw_c)::value;
+        constexpr bool FLOOD = decltype(flood_c)::value;
+        return [&](u32x4 b, uint32_t i0) {
             uint32_t key[4];
             bool pp[4], pb[4];
             uint64_t mp[4], mb[4];
             uint32_t tp = 0, tb = 0;
-            if (raw) {
-                // the signed compare of admit4_raw; admitted values are >= +0
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 4; ++u) {
+                if constexpr (RAW) {
                     pp[u] = static_cast<int32_t>(b[u]) >= static_cast<int32_t>(vt0);
-                    key[u] = b[u] ^ 0x7FFFFFFFu;
+                    key[u] = b[u] ^ 0x7FFFFFFFu;  // desc_key of a value >= +0
                     pb[u] = false;
-                    mp[u] = __builtin_amdgcn_ballot_w64(pp[u]);
-                    mb[u] = 0ull;
-                    tp += __builtin_popcountll(mp[u]);
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                } else {
                     key[u] = desc_key(b[u]);
                     pp[u] = key[u] <= T0;
                     pb[u] = DUAL && key[u] > T0 && key[u] <= T1;
-                    mp[u] = __builtin_amdgcn_ballot_w64(pp[u]);
-                    mb[u] = DUAL ? __builtin_amdgcn_ballot_w64(pb[u]) : 0ull;
-                    tp += __builtin_popcountll(mp[u]);
-                    tb += __builtin_popcountll(mb[u]);
                 }
+                mp[u] = __builtin_amdgcn_ballot_w64(pp[u]);
+                mb[u] = (DUAL && !RAW) ? __builtin_amdgcn_ballot_w64(pb[u]) : 0ull;
+                tp += __builtin_popcountll(mp[u]);
+                tb += __builtin_popcountll(mb[u]);
             }
             if (sp_n + sb_n + tp + tb <= static_cast<uint32_t>(kWaveCap)) {
                 // Staged in the wave's LDS share: primary upward, band downward.
@@ -1738,12 +1743,65 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 for (int u = 0; u < 4; ++u) {
                     if (pp[u]) stg[mbcnt_from(mp[u], sp_n)] = make_uint2(i0 + u, key[u]);
                     sp_n += __builtin_popcountll(mp[u]);
-                    if (DUAL) {
+                    if (DUAL && !RAW) {
                         if (pb[u]) stg[kWaveCap - 1 - mbcnt_from(mb[u], sb_n)] = make_uint2(i0 + u, key[u]);
                         sb_n += __builtin_popcountll(mb[u]);
                     }
                 }
                 return;
+            }
+            if constexpr (FLOOD) {
+                if (tp + tb >= 128u) {
+                    // Admission in bulk.  The key of the batch's first
+                    // candidate is tracked per part and kind; once the part
+                    // holds K stored copies of it, further copies are counted
+                    // out rather than stored.  Exact: any K equal keys are an
+                    // answer at a boundary (Sec. 4.4), and a copy left out has
+                    // K stored copies of its value, so the K-th largest of the
+                    // stored candidates and every candidate above it are those
+                    // of all the candidates; a part that leaves one out holds
+                    // >= K, so certification decides as before.
+                    uint64_t mm[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) mm[u] = mp[u] | mb[u];
+                    const int uf = mm[0] ? 0 : mm[1] ? 1 : mm[2] ? 2 : 3;
+                    const uint32_t lf = static_cast<uint32_t>(__builtin_ctzll(mm[uf]));
+                    const uint32_t kv = uf == 0 ? key[0] : uf == 1 ? key[1] : uf == 2 ? key[2] : key[3];
+                    const uint32_t kf = static_cast<uint32_t>(
+                        __builtin_amdgcn_readlane(static_cast<int>(kv), static_cast<int>(lf)));
+                    const int kind = (mp[uf] >> lf) & 1ull ? 0 : 1;
+                    bool eq[4];
+                    uint64_t me[4];
+                    uint32_t ne = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        eq[u] = (kind ? pb[u] : pp[u]) && key[u] == kf;
+                        me[u] = __builtin_amdgcn_ballot_w64(eq[u]);
+                        ne += __builtin_popcountll(me[u]);
+                    }
+                    if (ne >= 64u && kf != kNoElem) {
+                        // full[kind]: a key this wave already saw reach K
+                        // stored copies in the part (the count only grows)
+                        uint32_t drop = kf == full[kind] ? 1u : 0u;
+                        if (!drop) {
+                            if (lane() == 0) {
+                                const uint32_t cur = atomicCAS(&sm.fkey[kind], kNoElem, kf);
+                                if (cur == kNoElem || cur == kf) drop = atomicAdd(&sm.fcnt[kind], ne) >= k;
+                            }
+                            drop = readlane(drop, 0);
+                            if (drop) full[kind] = kf;
+                        }
+                        if (drop) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                if (kind) { pb[u] = pb[u] && !eq[u]; mb[u] &= ~me[u]; }
+                                else { pp[u] = pp[u] && !eq[u]; mp[u] &= ~me[u]; }
+                            }
+                            if (kind) tb -= ne; else tp -= ne;
+                            if (tp + tb == 0) return;
+                        }
+                    }
+                }
             }
             // kind 0: primary, upward from lo; kind 1: band, downward from hi - 1
             auto emit = [&](const bool (&pr)[4], int kind) {
@@ -1771,15 +1829,61 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             };
             wspill = true;
             emit(pp, 0);
-            if (DUAL) emit(pb, 1);
+            if (DUAL && !RAW) emit(pb, 1);
+        };
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    // Dual-boundary plans have no raw form and no flood form: their band
+    // makes a second classification per score, and three chunk loops in one
+    // kernel spill registers.
+    scan_span_sel<kSegVec, DUAL ? 1 : 3>(
+        sp,
+        [&]() {
+            if (!hinted) {
+                view_batch(x, g.a, g.nv, S, 0u, vb);
+                __builtin_amdgcn_s_waitcnt(0);
+            }
         },
+        [&]() {
+            clear_hist(h0);
+            if (threadIdx.x == 0) {
+                sm.cnt[0] = 0;
+                sm.cnt[1] = 0;
+                sm.kext[0] = kNoElem;
+                sm.kext[1] = 0;
+                sm.spilled = 0;
+                sm.fkey[0] = kNoElem;
+                sm.fkey[1] = kNoElem;
+                sm.fcnt[0] = 0;
+                sm.fcnt[1] = 0;
+            }
+            __syncthreads();
+            bool flood = false;
+            if (hinted) {
+                T0 = hkey;  // the proposal replaces Phase 1; no band
+                T1 = hkey;
+            } else {
+                const Cuts c = phase1(x, g.a, g.nv, S, g.q, g.q1, h0, sm, vb);
+                T0 = c.t0;
+                T1 = c.t1;
+                // samples at or above the primary boundary's coarse bin
+                const uint32_t b0 = readfirst(sm.res[0]);
+                flood = readfirst(sm.res[1]) + readfirst(h0[b0]) > 8u * g.q;
+            }
+            vt0 = T0 ^ 0x7FFFFFFFu;
+            mode = DUAL ? 1 : flood ? 2 : T0 <= 0x7FFFFFFFu ? 0 : 1;
+        },
+        [&]() { return mode; },
+        step(std::integral_constant<bool, !DUAL>{}, F_{}), step(F_{}, F_{}),
+        step(F_{}, std::integral_constant<bool, !DUAL>{}),
         NoPre{});
     // Flush the staged entries: one reservation per wave and kind, then
     // coalesced stores.  Each wave reads back only its own share.  Plain
     // (cached) stores: the row's finisher runs on the same XCD and reads
     // them back from its L2 (nontemporal stores cost it 0.5 us on decode).
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    {
+    if (mode != 2) {
         uint32_t pbase = 0, bbase = 0;
         if (lane() == 0) {
             if (sp_n) pbase = atomicAdd(&sm.cnt[0], sp_n);
@@ -1791,14 +1895,46 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
             const uint2 v = stg[e];
             region[lo + pbase + e] = v;
         }
-        if (wspill && lane() == 0) sm.spilled = 1;
         if (DUAL) {
             for (uint32_t e = lane(); e < sb_n; e += 64) {
                 const uint2 v = stg[kWaveCap - 1 - e];
                 region[hi - 1 - (bbase + e)] = v;
             }
         }
+    } else {
+        // Staged copies of a flood key that already has K stored copies in
+        // the part are left out as in the scan (the count only grows, so a
+        // value read while other waves still scan is a valid lower bound).
+        auto flush = [&](int kind, uint32_t n) {
+            if (n == 0) return;
+            const uint32_t dk = readfirst(sm.fcnt[kind]) >= k ? readfirst(sm.fkey[kind]) : kNoElem;
+            auto at = [&](uint32_t e) { return stg[kind ? kWaveCap - 1 - e : e]; };
+            uint32_t keep = n;
+            if (dk != kNoElem) {
+                keep = 0;
+                for (uint32_t e0 = 0; e0 < n; e0 += 64) {
+                    const uint32_t e = e0 + lane();
+                    keep += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e < n && at(e).y != dk));
+                }
+            }
+            uint32_t base = 0;
+            if (lane() == 0 && keep) base = atomicAdd(&sm.cnt[kind], keep);
+            base = readlane(base, 0);
+            for (uint32_t e0 = 0; e0 < n; e0 += 64) {
+                const uint32_t e = e0 + lane();
+                uint2 v = make_uint2(0u, dk);
+                if (e < n) v = at(e);
+                const bool kp = e < n && v.y != dk;
+                const uint64_t m = __builtin_amdgcn_ballot_w64(kp);
+                const uint32_t slot = base + mbcnt(m);
+                if (kp) region[kind ? hi - 1 - slot : lo + slot] = v;
+                base += __builtin_popcountll(m);
+            }
+        };
+        flush(0, sp_n);
+        if (DUAL) flush(1, sb_n);
     }
+    if (wspill && lane() == 0) sm.spilled = 1;
     __syncthreads();
     // A part whose candidates overflowed its stage (a row whose tail is most
     // of the row) also publishes the key range of its primary candidates, so

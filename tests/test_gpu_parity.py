@@ -224,6 +224,53 @@ def test_tied_candidates_shortcut_boundary():
         note("routes %s" % st)
 
 
+def kv_part_counts(sel, m_cap: int, n: int, splits: int) -> np.ndarray:
+    """The per-part (primary, band) candidate counts a KV-split scan stored in
+    the workspace: after M_cap regions of 2 (n + 128) eight-byte pairs, two
+    words per part and row."""
+    base = 16 * m_cap * (n + 128)
+    words = sel.workspace[base:base + 8 * m_cap * splits].cpu().numpy().view(np.uint32)
+    return words.reshape(m_cap, splits, 2)
+
+
+def test_kv_flood_rows_store_at_most_k_copies():
+    """Constant, signed-zero and +inf-flood rows over several parts: each part
+    stores the first bulk batches of its flood key that reach K copies and
+    counts the rest out, and the answer stays exact (any K equal keys at the
+    boundary, Sec. 4.4).  Two interleaved floods and a dense run of distinct
+    values in one coarse bin take the same scan form and must stay exact."""
+    t = topkf()
+    k, n = 2048, 262144
+    rng = np.random.default_rng(21)
+    x = np.empty((8, n), dtype=np.float32)
+    x[0] = 1.0                                    # constant
+    x[1] = -0.0                                   # -0 flood with a few +0 above it
+    x[1, rng.choice(n, 40, replace=False)] = 0.0
+    x[2] = 0.0                                    # +0 flood
+    x[3] = np.inf                                 # +inf flood
+    x[4] = -np.inf                                # a few finite values above a -inf flood
+    x[4, rng.choice(n, 1500, replace=False)] = rng.random(1500).astype(np.float32)
+    x[5] = np.float32(0.5)                        # a tie flood after a run of distinct values
+    x[5, :3000] = rng.random(3000).astype(np.float32) + np.float32(1.0)
+    x[6] = np.where(rng.random(n) < 0.5, np.float32(1.0), np.float32(2.0))  # two floods interleaved
+    x[7] = np.float32(1.0) + np.float32(0.03) * rng.random(n).astype(np.float32)  # one coarse bin, distinct
+    ke = np.array([n, n - 3, 200001, n - 77, n, 150004, n - 9, n], dtype=np.int32)
+    for name, P in (("kv-p4", 4), ("kv-p8", 8)):
+        plan = t.make_plan(t.FAMILY_KVSPLIT, 128, 0, splits=P, min_segment=4096)
+        note("flood rows plan %s" % name)
+        out, st, sel = run_topk(x, ke, k, plan=plan, stats=True)
+        assert_exact(out, x, ke, k)
+        cnt = kv_part_counts(sel, x.shape[0], n, P)
+        # bulk copies: K plus one batch; partial and mixed batches: a few per
+        # wave and segment end; plus the distinct run of row 5
+        bound = k + 8 * 256 + 2 * 512
+        for r in (0, 1, 2, 3, 4):
+            assert int(cnt[r, :, 0].max()) <= bound, (r, cnt[r, :, 0])
+            assert int(cnt[r, :, 0].sum()) >= k, (r, cnt[r, :, 0])
+        assert int(cnt[5, :, 0].max()) <= bound + 3000, cnt[5, :, 0]
+        note("routes %s" % st)
+
+
 def test_kv_finisher_slot_layouts():
     """The KV-split finisher maps each part's candidates to fixed register
     slots when no part holds more than its share, and searches the part
