@@ -342,8 +342,9 @@ __device__ __forceinline__ void lds_add(uint32_t* h, uint32_t bin, uint32_t v) {
     __hip_atomic_fetch_add(h + bin, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Histogram count for the lanes with pred; when they all hit one bin (constant
-// or heavily tied rows) a single add replaces 64 colliding LDS atomics.
+// Histogram count for the lanes with pred (m = their ballot, nonzero); when
+// they all hit one bin (constant or heavily tied rows) a single add replaces
+// up to 64 LDS atomics on one address, which the LDS would serialize.
 __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin, bool pred, uint64_t m) {
     const int leader = __builtin_ctzll(m);
     const uint32_t b0 = readlane(bin, leader);
@@ -352,6 +353,12 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin, bool pred, u
     } else if (pred) {
         lds_inc(h, bin);
     }
+}
+
+// hist_add over the lanes with `on` (any of them, or none).
+__device__ __forceinline__ void hist_count(uint32_t* h, uint32_t bin, bool on) {
+    const uint64_t m = __ballot(on);
+    if (m) hist_add(h, bin, on, m);
 }
 
 __device__ __forceinline__ u32x2 nt_load2(const uint2* p) {
@@ -1105,9 +1112,23 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hA, uint32_t*
         const uint32_t span = hi - lo;
         const uint32_t bl = span ? 32u - static_cast<uint32_t>(__builtin_clz(span)) : 0u;
         const uint32_t sh = bl > 11 ? bl - 11 : 0u;
+        {
+            // A wave whose first two slots each fall in one bin counts with
+            // hist_count (heavily tied rows would otherwise send 64 atomics
+            // to one address per slot); other waves use plain atomics.
+            const uint32_t d0 = (key[0] - lo) >> sh, d1 = (key[1] - lo) >> sh;
+            const bool a0 = act & 1u, a1 = (act >> 1) & 1u;
+            const bool tied = __ballot(a0) != 0 && __ballot(a0 && d0 != readfirst(d0)) == 0 &&
+                              __ballot(a1 && d1 != readfirst(d1)) == 0;
+            if (tied) {
 #pragma unroll
-        for (int u = 0; u < R; ++u)
-            if ((act >> u) & 1u) lds_inc(hA, (key[u] - lo) >> sh);
+                for (int u = 0; u < R; ++u) hist_count(hA, (key[u] - lo) >> sh, (act >> u) & 1u);
+            } else {
+#pragma unroll
+                for (int u = 0; u < R; ++u)
+                    if ((act >> u) & 1u) lds_inc(hA, (key[u] - lo) >> sh);
+            }
+        }
         clear_hist(hB);  // the next round's histogram, or the boundary list
         __syncthreads();
         const uint32_t t[1] = {kq};
@@ -2582,9 +2603,15 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         // round, and 2K is 4 % faster than 1.75K (2.25K no faster).
         r.primary_quarters = 8;
     } else {
-        // Parts per row: enough to fill the pool, but no segment shorter
-        // than 16K columns (shorter segments lose more to the replicated
-        // view than they gain in span).
+        // Parts per row: enough to fill the pool twice over, but no segment
+        // shorter than 16K columns (shorter segments lose more to the
+        // replicated view than they gain in span).  With ragged rows a part
+        // streams its segment at the rate one workgroup sustains, so the
+        // longest rows need several parts even when that overfills the pool
+        // and later parts wait for a slot (measured on 256 rows of up to 256K
+        // columns: 2 parts 95.7 us, 4 parts 80.0 us, 8 parts 81.4 us, 16 parts
+        // 89.0 us); decode and few-long-row shapes reach the segment floor
+        // first and are unchanged.
         r.family = TOPKF_FAMILY_KVSPLIT;
         // Primary boundary only, at K~ = 2K.  Collecting the band in the
         // fused pass costs every part a second classification of every
@@ -2596,7 +2623,7 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         // the exact coarse route, so the result stays exact.
         r.dual = 0;
         r.primary_quarters = 8;
-        int64_t P = (pool + rows - 1) / rows;
+        int64_t P = (2 * pool + rows - 1) / rows;
         int64_t pmax = (n + r.min_segment - 1) / r.min_segment;
         if (pmax > kMaxSplits) pmax = kMaxSplits;
         if (P > pmax) P = pmax;

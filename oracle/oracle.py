@@ -55,6 +55,9 @@ def _load():
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p]
+        lib.oracle_coarse_check.restype = ctypes.c_int64
+        lib.oracle_coarse_check.argtypes = [ctypes.c_uint32, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_int32, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -152,3 +155,21 @@ def check_rows(out: np.ndarray, x: np.ndarray, res: OracleResult,
             if len(fails) >= max_report:
                 break
     return fails
+
+
+def coarse_check(start: int, got: np.ndarray, threads: int | None = None) -> tuple[int, int | None]:
+    """Compares got[i] with c(x) of float32 pattern start + i (Sec. 4.2, Eq. 11;
+    the host CPU's IEEE round-to-nearest-even binary16 conversion), NaN
+    patterns skipped.  Returns (mismatches, first mismatching pattern or None).
+    Raises RuntimeError when the host CPU has no F16C conversion."""
+    got = np.ascontiguousarray(got, dtype=np.uint16)
+    if start < 0 or start + got.size > 1 << 32:
+        raise ValueError("pattern range outside 32 bits")
+    first = np.zeros(1, dtype=np.uint32)
+    r = _load().oracle_coarse_check(start, got.size, got.ctypes.data,
+                                    threads or default_threads(), first.ctypes.data)
+    if r == -1:
+        raise RuntimeError("the host CPU has no F16C conversion")
+    if r < 0:
+        raise ValueError("oracle_coarse_check: bad arguments")
+    return int(r), (int(first[0]) if r else None)

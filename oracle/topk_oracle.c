@@ -158,3 +158,83 @@ int oracle_topk(const float* x, int64_t m, int64_t n, int64_t stride, const int3
     pthread_mutex_destroy(&jb.mu);
     return jb.failed ? -2 : 0;
 }
+
+/*
+ * Coarse key c(x) of Sec. 4.2, Eq. 11, checked against a device's values for
+ * every float32 bit pattern in [start, start + n):
+ *   h  = the binary16 pattern of x under IEEE round-to-nearest-even (the
+ *        host CPU's F16C conversion, _mm256_cvtps_ph with rounding mode 0);
+ *   k  = h ^ 0x7FFF when the sign bit is clear, h when it is set (a larger
+ *        value gets a smaller key);
+ *   c  = k >> 5 (its top 11 bits).
+ * got[i] is the device's c for pattern start + i.  NaN patterns are skipped
+ * (the operator contract excludes NaN).  Returns the number of mismatches and
+ * sets *first to the first mismatching pattern (unchanged when none); -1 when
+ * the host CPU lacks F16C, -2 on bad arguments.
+ */
+#include <immintrin.h>
+
+typedef struct {
+    uint32_t start;
+    int64_t lo, hi;
+    const uint16_t* got;
+    int64_t bad;
+    int64_t first;  /* offset of the first mismatch, or -1 */
+} coarse_job;
+
+__attribute__((target("avx,f16c")))
+static void* coarse_worker(void* arg) {
+    coarse_job* j = (coarse_job*)arg;
+    j->bad = 0;
+    j->first = -1;
+    for (int64_t i = j->lo; i < j->hi; i += 8) {
+        uint32_t pat[8];
+        int cnt = (int)(j->hi - i < 8 ? j->hi - i : 8);
+        for (int u = 0; u < 8; ++u) pat[u] = j->start + (uint32_t)(i + (u < cnt ? u : 0));
+        __m256 v;
+        memcpy(&v, pat, sizeof pat);
+        const __m128i hv = _mm256_cvtps_ph(v, 0);  /* 0: round to nearest even */
+        uint16_t h[8];
+        memcpy(h, &hv, sizeof h);
+        for (int u = 0; u < cnt; ++u) {
+            if ((pat[u] & 0x7FFFFFFFu) > 0x7F800000u) continue;  /* NaN */
+            const uint32_t k16 = (h[u] & 0x8000u) ? h[u] : (uint32_t)(h[u] ^ 0x7FFFu);
+            if ((k16 >> 5) != j->got[i + u]) {
+                if (j->first < 0) j->first = i + u;
+                ++j->bad;
+            }
+        }
+    }
+    return NULL;
+}
+
+int64_t oracle_coarse_check(uint32_t start, int64_t n, const uint16_t* got, int32_t nthreads,
+                            uint32_t* first) {
+    if (n < 0 || n > ((int64_t)1 << 32) - (int64_t)start || (n > 0 && !got) || !first ||
+        nthreads < 1)
+        return -2;
+    __builtin_cpu_init();
+    if (!__builtin_cpu_supports("f16c") || !__builtin_cpu_supports("avx")) return -1;
+    int nt = nthreads > 256 ? 256 : nthreads;
+    coarse_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    const int64_t per = (n + nt - 1) / nt;
+    for (int t = 0; t < nt; ++t) {
+        jobs[t].start = start;
+        jobs[t].lo = per * t < n ? per * t : n;
+        jobs[t].hi = per * (t + 1) < n ? per * (t + 1) : n;
+        jobs[t].got = got;
+        started[t] = pthread_create(&th[t], NULL, coarse_worker, &jobs[t]) == 0;
+        if (!started[t]) coarse_worker(&jobs[t]);
+    }
+    int64_t bad = 0;
+    int64_t firsti = -1;
+    for (int t = 0; t < nt; ++t) {
+        if (started[t]) pthread_join(th[t], NULL);
+        bad += jobs[t].bad;
+        if (jobs[t].first >= 0 && (firsti < 0 || jobs[t].first < firsti)) firsti = jobs[t].first;
+    }
+    if (firsti >= 0) *first = start + (uint32_t)firsti;
+    return bad;
+}

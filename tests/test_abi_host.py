@@ -80,6 +80,8 @@ def test_planner_maps_workload_shapes():
         if fam == topkf.FAMILY_PERSISTENT:
             assert pl.workers == min(m, 2 * cus)
     assert long_.splits == 32 and decode.splits == 8
+    # ragged mid-size rows: parts for twice the pool, the longest rows split 4 ways
+    assert topkf.plan_for(256, 262144, cus).splits == 4
     assert decode.dual == 0 and decode.primary_quarters == 8
     assert prefill.primary_quarters == 8 and prefill.band_quarters == 10
 

@@ -163,6 +163,35 @@ def test_coarse_keys_match_ieee_fp16():
     assert want[x == np.inf].tolist() == [31] * int((x == np.inf).sum())
 
 
+def test_coarse_keys_exhaustive():
+    """Eq. 11 on the device for every float32 bit pattern (NaNs excluded), in
+    chunks of 2^28, against the C oracle's IEEE round-to-nearest-even binary16
+    conversion on the host CPU (itself pinned to numpy's conversion)."""
+    import torch
+    from oracle import oracle
+    t = T()
+    d = dev()
+    chunk = 1 << 28
+    base = torch.arange(chunk, dtype=torch.int64, device=d)
+    kd = torch.empty(chunk, dtype=torch.int16, device=d)
+    host = torch.empty(chunk, dtype=torch.int16, pin_memory=True)
+    for c in range((1 << 32) // chunk):
+        start = c * chunk
+        v = base + start
+        pats = torch.where(v >= 1 << 31, v - (1 << 32), v).to(torch.int32)
+        del v
+        t.coarse_keys(pats.view(torch.float32), kd)
+        host.copy_(kd)
+        torch.cuda.synchronize()
+        del pats
+        try:
+            bad, first = oracle.coarse_check(start, host.numpy().view(np.uint16))
+        except RuntimeError as e:
+            pytest.skip(str(e))
+        note("coarse keys patterns [%#010x, %#010x): %d mismatches" % (start, start + chunk, bad))
+        assert bad == 0, "first mismatch at pattern %#010x" % first
+
+
 def test_read_probe():
     """The streaming-read reference: validates alignment and size, reads a
     buffer without writing its sink for ordinary data."""

@@ -264,3 +264,66 @@ def test_checker_strict_set_with_equal_multiset():
     assert chk([0, 1, 3]) is None
     assert chk([0, 1, 4]) is None
     assert chk([0, 2, 3]) is not None
+
+
+# ------------------------------------------------- c(x) reference (Eq. 11)
+
+def _numpy_coarse(bits: np.ndarray) -> np.ndarray:
+    """c(x) from numpy's own IEEE round-to-nearest-even float32 -> float16
+    conversion (a software routine, independent of the host's F16C unit)."""
+    with np.errstate(over="ignore"):
+        h = bits.view(np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
+    return (np.where(h & 0x8000, h, h ^ 0x7FFF) >> 5).astype(np.uint16)
+
+
+def _windows() -> list[tuple[int, int]]:
+    """Pattern ranges around every place the conversion changes regime: the
+    signed zeros, the binary16 subnormal/normal boundary and smallest
+    subnormal, the overflow threshold 65520 (and 65504 below it), the
+    infinities and the first NaN patterns, and the ends of the pattern space."""
+    centers = [0x00000000, 0x33000000, 0x33800000, 0x387FE000, 0x38800000, 0x3F800000,
+               0x477FE000, 0x477FF000, 0x47800000, 0x7F800000, 0xFFFFFFFF - 4096]
+    out = []
+    for c in centers:
+        for sign in (0, 0x80000000):
+            lo = max(0, min((c | sign) - 4096, (1 << 32) - 8192))
+            out.append((lo, 8192))
+    return out
+
+
+def test_coarse_check_matches_numpy_fp16():
+    """The C reference behind the exhaustive device pin of c(x) agrees with
+    numpy's conversion on every boundary window and 4M random patterns."""
+    try:
+        for start, n in _windows():
+            bits = (np.arange(n, dtype=np.uint64) + start).astype(np.uint32)
+            keep = (bits & 0x7FFFFFFF) <= 0x7F800000
+            want = _numpy_coarse(bits)
+            want[~keep] = 0   # NaN patterns are skipped by the checker
+            assert oracle.coarse_check(start, want) == (0, None), hex(start)
+        rng = np.random.default_rng(17)
+        for _ in range(4):
+            start = int(rng.integers(0, (1 << 32) - (1 << 20)))
+            bits = (np.arange(1 << 20, dtype=np.uint64) + start).astype(np.uint32)
+            assert oracle.coarse_check(start, _numpy_coarse(bits))[0] == 0
+    except RuntimeError as e:
+        pytest.skip(str(e))
+
+
+def test_coarse_check_finds_planted_mismatches():
+    """One flipped key is counted and located; NaN patterns are not compared."""
+    try:
+        start = 0x47000000
+        bits = (np.arange(1 << 16, dtype=np.uint64) + start).astype(np.uint32)
+        got = _numpy_coarse(bits)
+        got[777] ^= 1
+        got[40000] += 3
+        assert oracle.coarse_check(start, got) == (2, start + 777)
+        nan_start = 0x7F800001
+        assert oracle.coarse_check(nan_start, np.full(4096, 123, dtype=np.uint16)) == (0, None)
+        # +inf: 0x7C00 ^ 0x7FFF = 0x03FF -> 31, and 65520 rounds up to +inf;
+        # just below 65520 rounds to 65504 = 0x7BFF -> 0x0400 -> 32
+        got = _numpy_coarse(np.array([0x7F800000, 0x477FF000, 0x477FEFFF], dtype=np.uint32))
+        assert got.tolist() == [31, 31, 32]
+    except RuntimeError as e:
+        pytest.skip(str(e))
