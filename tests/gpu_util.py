@@ -86,3 +86,36 @@ def auto_plan(m: int, n: int):
     from exact_row_wise_sampled_amd import topkf
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     return topkf.plan_for(m, n, cus)
+
+
+def view_phase(row: int, s: int) -> int:
+    """The row's view residue: log2(s)-bit reversal of row mod s (Eq. 13 reading)."""
+    b = s.bit_length() - 1
+    r = row % s
+    return int(format(r, "0%db" % b)[::-1], 2)
+
+
+def aliased_rows(s: int, k: int, n: int, m: int, kind: str, seed: int = 0):
+    """Rows whose view (residue a_r) sees a misleading tail.
+
+    'band':  q view entries at 100, the next q1-q view entries at 50, and
+             enough 50s elsewhere that the secondary boundary certifies.
+    'exact': q view entries at 100 and q1-q at 50, all other values small, so
+             both boundaries underfill and exact recovery must run.
+    """
+    rng = np.random.default_rng(seed)
+    cdiv = lambda a, b: -(-a // b)
+    q = cdiv(cdiv(3 * k, 2), s)
+    q1 = cdiv(cdiv(7 * k, 4), s)
+    x = (rng.standard_normal((m, n)) * 0.1).astype(np.float32)
+    for r in range(m):
+        a = view_phase(r, s)
+        view = np.arange(a, n, s)
+        x[r, view[:q]] = 100.0 + rng.random(q).astype(np.float32)
+        x[r, view[q:q1]] = 50.0 + rng.random(q1 - q).astype(np.float32)
+        if kind == "band":
+            others = np.setdiff1d(np.arange(n), view)
+            pick = rng.choice(others, size=2 * k, replace=False)
+            x[r, pick] = 50.0 + rng.random(2 * k).astype(np.float32)
+    ke = np.full(m, n, dtype=np.int32)
+    return x, ke
