@@ -5,22 +5,28 @@
 // One 512-thread workgroup (8 wave64) works on a row (or a row segment):
 //   Phase 1 (Sec. 4.2, Eqs. 11-15; Sec. 5.2): the regular view
 //     V = {i < L : i = a_r mod s} is projected to the 11-bit coarse key and
-//     histogrammed in LDS; the first bins whose prefix reaches q = ceil(1.5K/s)
-//     and q1 = ceil(1.75K/s) give tau0 and tau1, converted once to inclusive
-//     FP32 cutoffs expressed as descending integer keys.  The first chunk of
-//     the complete-row scan is already in flight while the view is loaded.
+//     histogrammed in LDS; the first bins whose prefix reaches
+//     q = ceil(K~/s) and q1 = ceil(K~1/s) give tau0 and tau1 (the plan sets
+//     K~ and K~1 in quarters of K), converted once to inclusive FP32 cutoffs
+//     expressed as descending integer keys.  The row's first loads are
+//     already in flight while the view is histogrammed.
 //   Phase 2 (Sec. 4.3, Eqs. 16-17; Sec. 5.3): one streaming pass over the
-//     row with 128-bit nontemporal loads admits key <= T0, appends the
-//     (index, key) pair to the frontier and counts its leading 11-bit digit.
-//     Underfill (C < K) adds the band T0 < key <= T1 (Eqs. 18-19); continued
-//     underfill, an unusable view or the no-view policy take the exact coarse
-//     route (Eq. 20).
-//   Phase 3 (Sec. 4.4, Eqs. 22-25; Sec. 5.4): 11+11+10-bit refinement of the
-//     FP32 descending key over the frontier only, through two ping-pong
-//     buffers of (index, key) pairs (LDS first, then a global spill slice).
+//     row with 128-bit nontemporal loads admits key <= T0 and appends the
+//     (index, key) pair to the frontier.  Underfill (C < K) adds the band
+//     T0 < key <= T1 (Eqs. 18-19); continued underfill, an unusable view or
+//     the no-view policy take the exact coarse route (Eq. 20).
+//   Phase 3 (Sec. 4.4, Eqs. 22-25; Sec. 5.4): radix refinement of the FP32
+//     descending key over the frontier only, from registers (a digit window
+//     of at most 11 bits over the frontier's key range, at most three rounds)
+//     or, for frontiers beyond registers, 11+11+10-bit digits through two
+//     ping-pong buffers of (index, key) pairs (LDS first, then a global
+//     spill slice).
 // Two mappings (Sec. 4.5, Sec. 5.5): a persistent pool whose workgroups take
 // rows from a device queue, and a KV-split mapping in which P workgroups scan
-// disjoint segments of one row and the last to arrive finishes it.
+// disjoint segments of one row (kvsplit_scan_kernel) and a second kernel on
+// the same stream merges their counts and candidates and finishes each row
+// (kvsplit_finish_kernel): the kernel boundary makes every part's writes
+// visible without a per-workgroup cache write-back.
 //
 // Every wave of a workgroup runs the same trip counts, so the ballots below
 // always see all 64 lanes.
