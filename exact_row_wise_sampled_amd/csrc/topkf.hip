@@ -103,6 +103,8 @@ struct alignas(16) Shared {
     alignas(16) uint32_t wsum[3][kWaves];  // per-wave totals: [0] block_find, [1], [2] scans
     uint32_t wcnt[kWaves];             // wave-private frontier sizes
     uint32_t res[4];
+    uint32_t rcnt[2];                  // block_find: the count of each target's bin
+    alignas(16) uint32_t wext[2][kWaves];  // per-wave smallest and largest key
     uint32_t cnt[2];
     uint32_t out_cnt;
     uint32_t tie_cnt;
@@ -110,7 +112,6 @@ struct alignas(16) Shared {
     int32_t next_row;
     uint32_t part_max;  // KV-split finisher: the largest candidate count of one part
     uint32_t kext[2];  // smallest and largest key of a large frontier
-    uint32_t small_n;  // register refinement: entries in the small boundary list
     uint32_t spilled;  // KV-split scan: some wave wrote candidates past its stage
     uint32_t fkey[2];  // KV-split scan: the part's flood key per kind (kNoElem: none yet)
     uint32_t fcnt[2];  // KV-split scan: copies of it in bulk batches so far
@@ -551,7 +552,8 @@ __device__ __forceinline__ void clear_hist(uint32_t* h) {
 }
 
 // For each target t[i] (1 <= t[i] <= sum of hist), finds b = min{b : H(b) >=
-// t[i]} and H(b - 1) (Eqs. 15, 23), written to sm.res[2i], sm.res[2i + 1].
+// t[i]} and H(b - 1) (Eqs. 15, 23), written to sm.res[2i], sm.res[2i + 1],
+// and the count of bin b, written to sm.rcnt[i].
 // Each thread owns 4 consecutive bins.  Reads hist before its first barrier
 // and ends with a barrier, so hist may be rewritten right after it returns.
 template <int NT>
@@ -562,7 +564,7 @@ __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t 
     // excludes); the finding thread overwrites them after the first barrier.
     if (tid == 0) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i) { sm.res[2 * i] = kBins - 1; sm.res[2 * i + 1] = 0; }
+        for (int i = 0; i < NT; ++i) { sm.res[2 * i] = kBins - 1; sm.res[2 * i + 1] = 0; sm.rcnt[i] = 0; }
     }
     const uint4 v = reinterpret_cast<const uint4*>(hist)[tid];
     const uint32_t s = v.x + v.y + v.z + v.w;
@@ -574,16 +576,17 @@ __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t 
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         if (excl < t[i] && t[i] <= excl + s) {
-            uint32_t acc = excl, b = 4 * tid;
+            uint32_t acc = excl, b = 4 * tid, c = v.x;
             if (acc + v.x < t[i]) {
-                acc += v.x; b += 1;
+                acc += v.x; b += 1; c = v.y;
                 if (acc + v.y < t[i]) {
-                    acc += v.y; b += 1;
-                    if (acc + v.z < t[i]) { acc += v.z; b += 1; }
+                    acc += v.y; b += 1; c = v.z;
+                    if (acc + v.z < t[i]) { acc += v.z; b += 1; c = v.w; }
                 }
             }
             sm.res[2 * i] = b;
             sm.res[2 * i + 1] = acc;
+            sm.rcnt[i] = c;
         }
     }
     __syncthreads();
@@ -1085,30 +1088,35 @@ template <int R, class Load>
 __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hA, uint32_t* hB, uint32_t kq,
                                             uint32_t out_base, int32_t* outp, uint32_t k,
                                             Shared& sm) {
+    // load(u, idx, key) issues its load unconditionally (a clamped address
+    // for a slot without an entry) and returns whether slot u holds one, so
+    // that the R loads of a thread are in flight together.
     uint32_t idx[R], key[R];
     uint32_t act = 0;
+#pragma unroll
+    for (int u = 0; u < R; ++u) act |= load(u, idx[u], key[u]) ? 1u << u : 0u;
     uint32_t mn = kNoElem, mx = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-        idx[u] = 0;
-        key[u] = kNoElem;
-        if (load(u, idx[u], key[u])) {
-            act |= 1u << u;
-            mn = key[u] < mn ? key[u] : mn;
-            mx = key[u] > mx ? key[u] : mx;
-        }
+        const bool on = (act >> u) & 1u;
+        mn = on && key[u] < mn ? key[u] : mn;
+        mx = on && key[u] > mx ? key[u] : mx;
     }
-    if (threadIdx.x == 0) {
-        sm.small_n = 0;
-        sm.kext[0] = kNoElem;
-        sm.kext[1] = 0;
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane() == 0) {
+        sm.wext[0][wave()] = mn;
+        sm.wext[1][wave()] = mx;
     }
     clear_hist(hA);
-    __syncthreads();  // entries are in registers; the frontier buffer becomes the stage
-    lds_extremes(&sm.kext[0], mn, mx);
-    __syncthreads();
-    uint32_t lo = readfirst(sm.kext[0]);
-    uint32_t hi = readfirst(sm.kext[1]);
+    __syncthreads();  // entries are in registers (the frontier buffer becomes the stage)
+    uint32_t lo, hi;
+    {
+        const uint4* we = reinterpret_cast<const uint4*>(&sm.wext[0][0]);
+        const uint4 a = we[0], b = we[1], c = we[2], d = we[3];
+        lo = min(min(min(a.x, a.y), min(a.z, a.w)), min(min(b.x, b.y), min(b.z, b.w)));
+        hi = max(max(max(c.x, c.y), max(c.z, c.w)), max(max(d.x, d.y), max(d.z, d.w)));
+    }
     uint32_t* stage = reinterpret_cast<uint32_t*>(sm.front);
     const uint32_t base0 = out_base;
     // Each round at least halves the window's bit length in the worst case
@@ -1139,73 +1147,71 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hA, uint32_t*
         __syncthreads();
         const uint32_t t[1] = {kq};
         block_find<1>(hA, t, sm);
-        const uint32_t b = sm.res[0], before = sm.res[1];
-        const uint32_t inb = hA[b];
+        const uint32_t b = sm.res[0], before = sm.res[1], inb = sm.rcnt[0];
         const bool exact_fill = before + inb == kq;  // the boundary group fits exactly
         const bool last = exact_fill || sh == 0;
+        const bool small = !last && inb <= 64;
         const uint32_t need = kq - before;
-        uint32_t com = 0, tie = 0, keep = 0;
+        // com: committed entries; grp: the boundary bin's entries (ties
+        // filling the last slots after a last round, else kept)
+        uint32_t com = 0, grp = 0;
 #pragma unroll
         for (int u = 0; u < R; ++u) {
             const uint32_t d = (key[u] - lo) >> sh;
             const bool on = (act >> u) & 1u;
             if (on && (d < b || (exact_fill && d == b))) com |= 1u << u;
-            if (on && !exact_fill && d == b) {
-                if (last) tie |= 1u << u;
-                else keep |= 1u << u;
-            }
+            if (on && !exact_fill && d == b) grp |= 1u << u;
         }
         uint32_t tot;
         const uint32_t ex = block_excl_scan(
             static_cast<uint32_t>(__builtin_popcount(com)) |
-                (static_cast<uint32_t>(__builtin_popcount(tie)) << 16),
+                (static_cast<uint32_t>(__builtin_popcount(grp)) << 16),
             &tot, sm, 1);
         const uint32_t tot_c = tot & 0xFFFFu;
-        uint32_t pc = out_base + (ex & 0xFFFFu);
-        uint32_t pt = ex >> 16;
+        const uint32_t pc0 = out_base + (ex & 0xFFFFu), pg0 = ex >> 16;
+        // A boundary group of at most 64 entries is finished by one wave:
+        // gathered into a list (in hB), each entry's rank among the group by
+        // full key (equal keys by list position) is its order, and the
+        // `need` first take the remaining slots: the selection the remaining
+        // rounds would make.
+        uint2* list = reinterpret_cast<uint2*>(hB);
 #pragma unroll
         for (int u = 0; u < R; ++u) {
+            const uint32_t below = (1u << u) - 1u;
             if ((com >> u) & 1u) {
+                const uint32_t pc = pc0 + static_cast<uint32_t>(__builtin_popcount(com & below));
                 if (pc < k) stage[pc] = idx[u];
-                ++pc;
             }
-            if ((tie >> u) & 1u) {
-                const uint32_t slot = out_base + tot_c + pt;
-                if (pt < need && slot < k) stage[slot] = idx[u];
-                ++pt;
+            if ((grp >> u) & 1u) {
+                const uint32_t pg = pg0 + static_cast<uint32_t>(__builtin_popcount(grp & below));
+                if (last) {
+                    const uint32_t slot = out_base + tot_c + pg;
+                    if (pg < need && slot < k) stage[slot] = idx[u];
+                } else if (small) {
+                    list[pg] = make_uint2(idx[u], key[u]);
+                }
             }
         }
         if (last) break;
-        if (inb <= 64) {
-            // A boundary group of at most 64 entries is finished by one wave:
-            // gathered into a list (in hB), each entry's rank among the group
-            // by full key (equal keys by list position) is its order, and the
-            // `need` first take the remaining slots.  The same selection the
-            // remaining rounds would make.
-            uint2* list = reinterpret_cast<uint2*>(hB);
-#pragma unroll
-            for (int u = 0; u < R; ++u) {
-                const bool kp = (keep >> u) & 1u;
-                const uint64_t m = __ballot(kp);
-                if (m) {
-                    const uint32_t base = wave_reserve(&sm.small_n, m, __builtin_popcountll(m));
-                    if (kp) list[base + mbcnt(m)] = make_uint2(idx[u], key[u]);
-                }
-            }
+        if (small) {
             __syncthreads();
             if (wave() == 0) {
                 const uint32_t l = lane();
                 const uint2 mine = l < inb ? list[l] : make_uint2(0u, kNoElem);
                 uint32_t rank = 0;
-                for (uint32_t e = 0; e < inb; ++e) {
-                    const uint32_t ke = readlane(mine.y, static_cast<int>(e));
-                    rank += (ke < mine.y || (ke == mine.y && e < l)) ? 1u : 0u;
+                for (uint32_t e0 = 0; e0 < inb; e0 += 8) {
+#pragma unroll
+                    for (uint32_t jj = 0; jj < 8; ++jj) {
+                        const uint32_t e = e0 + jj;
+                        const uint32_t ke = readlane(mine.y, static_cast<int>(e));
+                        rank += (e < inb && (ke < mine.y || (ke == mine.y && e < l))) ? 1u : 0u;
+                    }
                 }
                 if (l < inb && rank < need) stage[out_base + tot_c + rank] = mine.x;
             }
             break;
         }
-        act = keep;
+        act = grp;
         out_base += tot_c;
         kq = need;
         lo += b << sh;
@@ -1363,11 +1369,11 @@ __device__ __forceinline__ void finish_waves(uint32_t C, const uint2* spill_base
         refine_regs<kWaveRegs>(
             [&](int u, uint32_t& i, uint32_t& key) {
                 const uint32_t e = lane() + 64 * u;
-                if (e >= mine) return false;
-                const uint2 v = reg[e];
+                const bool on = e < mine;
+                const uint2 v = reg[on ? e : 0u];
                 i = v.x;
                 key = desc_key(v.y);
-                return true;
+                return on;
             },
             h1, h0, kq, out_base, outp, k, sm);
         return;
@@ -1994,19 +2000,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     const uint32_t per_xcd = gridDim.x / 8;
     const uint32_t row = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (row >= static_cast<uint32_t>(p.m_cap)) return;
-    // The live-row count, the row's length and the parts' counts are loaded
-    // together; counts of parts the row did not use this call are stale and
-    // are dropped below.
+    // The live-row count, the row's length and the parts' counts (wave 0,
+    // four parts per lane) are loaded together; counts of parts the row did
+    // not use this call are stale and are dropped below.
     const int32_t nvr = *p.num_valid_rows;
     const int32_t ke_row = p.ke[row];
     uint32_t hkey = 0;
     bool hinted = false;
     if constexpr (HINT) hinted = row_hint(p, row, &hkey);
     const uint32_t* counts = kv_counts(p, row);
-    uint32_t cp = 0, cb = 0;
-    if (threadIdx.x < static_cast<uint32_t>(p.splits)) {
-        cp = counts[2 * threadIdx.x];
-        cb = counts[2 * threadIdx.x + 1];
+    uint32_t c4[2][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const uint32_t pp = 4 * lane() + v;
+        c4[0][v] = 0;
+        c4[1][v] = 0;
+        if (wave() == 0 && pp < static_cast<uint32_t>(p.splits)) {
+            c4[0][v] = counts[2 * pp];
+            c4[1][v] = counts[2 * pp + 1];
+        }
     }
     const uint32_t m_live = clamp_len(nvr, p.m_cap);
     if (row >= m_live) return;
@@ -2021,24 +2033,39 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     uint32_t* h0 = sm.hist[0];
     uint32_t* h1 = sm.hist[1];
 
-    // Merge the parts (Eq. 27): prefix offsets of the primary and band counts.
-    if (threadIdx.x >= Pr) { cp = 0; cb = 0; }
-    if (threadIdx.x == 0) sm.part_max = 0;
+    // Merge the parts (Eq. 27): wave 0 forms the prefix offsets of the
+    // primary and band counts and the largest count of one part; one barrier
+    // publishes them.
+    if (wave() == 0) {
+        uint32_t mxp = 0;
+#pragma unroll
+        for (int kind = 0; kind < 2; ++kind) {
+            uint32_t s4 = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                if (4 * lane() + v >= Pr) c4[kind][v] = 0;
+                s4 += c4[kind][v];
+                mxp = c4[kind][v] > mxp ? c4[kind][v] : mxp;
+            }
+            const uint32_t incl = wave_incl_scan(s4);
+            uint32_t o = incl - s4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t pp = 4 * lane() + v;
+                if (pp < Pr) sm.offs[kind][pp] = o;
+                o += c4[kind][v];
+            }
+            if (lane() == 63) sm.offs[kind][Pr] = incl;
+        }
+        mxp = wave_max(mxp);
+        if (lane() == 0) {
+            sm.part_max = mxp;
+            sm.out_cnt = 0;
+        }
+    }
     clear_hist(h1);
-    uint32_t C0 = 0, CB = 0;
-    const uint32_t op = block_excl_scan(cp, &C0, sm, 1);
-    const uint32_t ob = block_excl_scan(cb, &CB, sm, 2);
-    if (threadIdx.x < Pr) { sm.offs[0][threadIdx.x] = op; sm.offs[1][threadIdx.x] = ob; }
-    {
-        const uint32_t mx = wave_max(cp > cb ? cp : cb);
-        if (lane() == 0 && mx) __hip_atomic_fetch_max(&sm.part_max, mx, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    if (threadIdx.x == 0) {
-        sm.offs[0][Pr] = C0;
-        sm.offs[1][Pr] = CB;
-        sm.out_cnt = 0;
-    }
+    __syncthreads();  // offsets visible
+    const uint32_t C0 = sm.offs[0][Pr], CB = sm.offs[1][Pr];
     int route = TOPKF_ROUTE_PRIMARY;
     uint32_t ctot = C0;
     if (C0 < k) {
@@ -2050,7 +2077,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         return;
     }
     count_route(p, route);
-    __syncthreads();  // offsets visible
     if (ctot <= static_cast<uint32_t>(kBlock * kRegs)) {
         // Register slots: when no part holds more than cap = 2^lc candidates
         // of a kind, with nr * cap <= kBlock * kRegs for the nr part ranges in
@@ -2064,16 +2090,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         uint32_t src[kRegs];
         bool live[kRegs];
         if (sm.part_max <= (1u << lc)) {
+            // every LDS read unconditional, so that they issue together
 #pragma unroll
             for (int u = 0; u < kRegs; ++u) {
                 const uint32_t gq = threadIdx.x + kBlock * u;
                 const uint32_t q = gq >> lc, j = gq & ((1u << lc) - 1u);
                 const uint32_t kind = q >= Pr ? 1u : 0u;
                 const uint32_t pp = q < nr ? q - kind * Pr : 0u;
-                live[u] = q < nr && j < sm.offs[kind][pp + 1] - sm.offs[kind][pp];
+                const uint32_t* o = sm.offs[kind] + pp;
+                const uint32_t n = o[1] - o[0];
+                live[u] = (q < nr) & (j < n);
                 const uint32_t s0 = pp * chunk;
                 const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
-                src[u] = kind ? s1 - 1 - j : s0 + j;
+                const uint32_t sv = kind ? s1 - 1 - j : s0 + j;
+                src[u] = live[u] ? sv : 0u;
             }
         } else {
             uint32_t pstep = 1;
@@ -2087,7 +2117,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                     const int kind = gi < C0 ? 0 : 1;
                     const uint32_t r = kind ? gi - C0 : gi;
                     const uint32_t cand = src[u] + step;
-                    if (gi < ctot && cand < Pr && sm.offs[kind][cand] <= r) src[u] = cand;
+                    const uint32_t ov = sm.offs[kind][cand < Pr ? cand : 0u];
+                    if (gi < ctot && cand < Pr && ov <= r) src[u] = cand;
                 }
             }
 #pragma unroll
@@ -2096,20 +2127,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 const int kind = gi < C0 ? 0 : 1;
                 const uint32_t r = kind ? gi - C0 : gi;
                 const uint32_t pp = src[u];
-                const uint32_t j = gi < ctot ? r - sm.offs[kind][pp] : 0;
+                const uint32_t ov = sm.offs[kind][pp];
+                live[u] = gi < ctot;
+                const uint32_t j = live[u] ? r - ov : 0u;
                 const uint32_t s0 = pp * chunk;
                 const uint32_t s1 = s0 + chunk < L ? s0 + chunk : L;
-                src[u] = kind ? s1 - 1 - j : s0 + j;
-                live[u] = gi < ctot;
+                const uint32_t sv = kind ? s1 - 1 - j : s0 + j;
+                src[u] = live[u] ? sv : 0u;
             }
         }
         refine_regs<kRegs>(
             [&](int u, uint32_t& i, uint32_t& key) {
-                if (!live[u]) return false;
                 const uint2 t2 = region[src[u]];
                 i = t2.x;
                 key = t2.y;
-                return true;
+                return live[u];
             },
             h1, h0, k, 0u, outp, k, sm);
         return;
@@ -2443,11 +2475,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         refine_regs<kRegs>(
             [&](int u, uint32_t& i, uint32_t& key) {
                 const uint32_t gi = threadIdx.x + kBlock * u;
-                if (gi >= nq) return false;
-                const uint2 t2 = region[gi];
+                const bool on = gi < nq;
+                const uint2 t2 = region[on ? gi : 0u];
                 i = t2.x;
                 key = t2.y;
-                return true;
+                return on;
             },
             h1, h0, kq, before, outp, k, sm);
         return;
