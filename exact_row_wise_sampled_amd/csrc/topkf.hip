@@ -362,10 +362,19 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin, bool pred, u
     }
 }
 
-// hist_add over the lanes with `on` (any of them, or none).
-__device__ __forceinline__ void hist_count(uint32_t* h, uint32_t bin, bool on) {
+// Histogram count for the lanes with `on`: the lanes that share the first
+// such lane's bin add their number with one atomic, the others one each (a
+// group of equal keys would otherwise send up to 64 atomics to one LDS
+// address, which the LDS serializes).
+__device__ __forceinline__ void hist_count_lead(uint32_t* h, uint32_t bin, bool on) {
     const uint64_t m = __ballot(on);
-    if (m) hist_add(h, bin, on, m);
+    if (m == 0) return;
+    const int leader = __builtin_ctzll(m);
+    const uint32_t b0 = readlane(bin, leader);
+    const bool same = on && bin == b0;
+    const uint64_t me = __ballot(same);
+    if (static_cast<int>(lane()) == leader) lds_add(h, b0, __builtin_popcountll(me));
+    else if (on && !same) lds_inc(h, bin);
 }
 
 __device__ __forceinline__ u32x2 nt_load2(const uint2* p) {
@@ -1127,16 +1136,21 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hA, uint32_t*
         const uint32_t bl = span ? 32u - static_cast<uint32_t>(__builtin_clz(span)) : 0u;
         const uint32_t sh = bl > 11 ? bl - 11 : 0u;
         {
-            // A wave whose first two slots each fall in one bin counts with
-            // hist_count (heavily tied rows would otherwise send 64 atomics
-            // to one address per slot); other waves use plain atomics.
-            const uint32_t d0 = (key[0] - lo) >> sh, d1 = (key[1] - lo) >> sh;
-            const bool a0 = act & 1u, a1 = (act >> 1) & 1u;
-            const bool tied = __ballot(a0) != 0 && __ballot(a0 && d0 != readfirst(d0)) == 0 &&
-                              __ballot(a1 && d1 != readfirst(d1)) == 0;
+            // A wave whose first slot has at least 8 lanes in the bin of its
+            // first active lane counts with hist_count_lead (heavily tied
+            // rows would otherwise send up to 64 atomics to one address per
+            // slot); other waves use plain atomics.
+            const uint32_t d0 = (key[0] - lo) >> sh;
+            const bool a0 = act & 1u;
+            const uint64_t m0 = __ballot(a0);
+            bool tied = false;
+            if (m0) {
+                const uint32_t b0 = readlane(d0, __builtin_ctzll(m0));
+                tied = __builtin_popcountll(__ballot(a0 && d0 == b0)) >= 8;
+            }
             if (tied) {
 #pragma unroll
-                for (int u = 0; u < R; ++u) hist_count(hA, (key[u] - lo) >> sh, (act >> u) & 1u);
+                for (int u = 0; u < R; ++u) hist_count_lead(hA, (key[u] - lo) >> sh, (act >> u) & 1u);
             } else {
 #pragma unroll
                 for (int u = 0; u < R; ++u)
