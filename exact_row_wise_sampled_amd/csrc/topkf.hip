@@ -112,7 +112,6 @@ struct alignas(16) Shared {
     int32_t next_row;
     uint32_t part_max;  // KV-split finisher: the largest candidate count of one part
     uint32_t kext[2];  // smallest and largest key of a large frontier
-    uint32_t spilled;  // KV-split scan: some wave wrote candidates past its stage
     uint32_t fkey[2];  // KV-split scan: the part's flood key per kind (kNoElem: none yet)
     uint32_t fcnt[2];  // KV-split scan: copies of it in bulk batches so far
     alignas(16) uint32_t hist[2][kBins];
@@ -1092,11 +1091,14 @@ __device__ __forceinline__ uint32_t exact_route(const float* x, uint32_t L, uint
 // from block prefix sums and are staged in LDS (the frontier buffer is free
 // once the entries are in registers), then written out with coalesced
 // stores.  hA, hB: two 2048-bin LDS histograms (any contents).  Writes
-// out[out_base, k).
-template <int R, class Load>
+// out[out_base, k).  KNOWN: the caller gives the entries' smallest and
+// largest key, has cleared hA and made it visible, and reads nothing from the
+// frontier buffer (it becomes the stage without a barrier).
+template <int R, bool KNOWN = false, class Load>
 __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hA, uint32_t* hB, uint32_t kq,
                                             uint32_t out_base, int32_t* outp, uint32_t k,
-                                            Shared& sm) {
+                                            Shared& sm, uint32_t lo_known = 0,
+                                            uint32_t hi_known = 0) {
     // load(u, idx, key) issues its load unconditionally (a clamped address
     // for a slot without an entry) and returns whether slot u holds one, so
     // that the R loads of a thread are in flight together.
@@ -1104,23 +1106,23 @@ __device__ __forceinline__ void refine_regs(Load&& load, uint32_t* hA, uint32_t*
     uint32_t act = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) act |= load(u, idx[u], key[u]) ? 1u << u : 0u;
-    uint32_t mn = kNoElem, mx = 0;
+    uint32_t lo = lo_known, hi = hi_known;
+    if constexpr (!KNOWN) {
+        uint32_t mn = kNoElem, mx = 0;
 #pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const bool on = (act >> u) & 1u;
-        mn = on && key[u] < mn ? key[u] : mn;
-        mx = on && key[u] > mx ? key[u] : mx;
-    }
-    mn = wave_min(mn);
-    mx = wave_max(mx);
-    if (lane() == 0) {
-        sm.wext[0][wave()] = mn;
-        sm.wext[1][wave()] = mx;
-    }
-    clear_hist(hA);
-    __syncthreads();  // entries are in registers (the frontier buffer becomes the stage)
-    uint32_t lo, hi;
-    {
+        for (int u = 0; u < R; ++u) {
+            const bool on = (act >> u) & 1u;
+            mn = on && key[u] < mn ? key[u] : mn;
+            mx = on && key[u] > mx ? key[u] : mx;
+        }
+        mn = wave_min(mn);
+        mx = wave_max(mx);
+        if (lane() == 0) {
+            sm.wext[0][wave()] = mn;
+            sm.wext[1][wave()] = mx;
+        }
+        clear_hist(hA);
+        __syncthreads();  // entries are in registers (the frontier buffer becomes the stage)
         const uint4* we = reinterpret_cast<const uint4*>(&sm.wext[0][0]);
         const uint4 a = we[0], b = we[1], c = we[2], d = we[3];
         lo = min(min(min(a.x, a.y), min(a.z, a.w)), min(min(b.x, b.y), min(b.z, b.w)));
@@ -1666,7 +1668,7 @@ __device__ __forceinline__ uint32_t* kv_counts(const Params& p, uint32_t row) {
 }
 
 // After every row's counts, two words per part: the smallest and largest key
-// among its primary candidates (read only for frontiers beyond registers).
+// among its stored primary candidates (kNoElem and 0 when it stored none).
 __device__ __forceinline__ uint32_t* kv_ext(const Params& p, uint32_t row) {
     return kv_counts(p, 0) + 2 * static_cast<int64_t>(p.m_cap) * p.splits +
            2 * static_cast<int64_t>(row) * p.splits;
@@ -1748,7 +1750,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     uint2* stg = sm.front + wave() * kWaveCap;
     uint32_t sp_n = 0, sb_n = 0;
     uint32_t pmin = kNoElem, pmax = 0;  // keys of primary candidates written directly
-    bool wspill = false;
     uint32_t vb[kSampleVec];
     const Span sp = make_span(x, lo, hi);
     uint32_t vt0 = 0;         // raw admission: signed-int form of the cutoff
@@ -1874,7 +1875,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                     base += __builtin_popcountll(m[u]);
                 }
             };
-            wspill = true;
             emit(pp, 0);
             if (DUAL && !RAW) emit(pb, 1);
         };
@@ -1899,7 +1899,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 sm.cnt[1] = 0;
                 sm.kext[0] = kNoElem;
                 sm.kext[1] = 0;
-                sm.spilled = 0;
                 sm.fkey[0] = kNoElem;
                 sm.fkey[1] = kNoElem;
                 sm.fcnt[0] = 0;
@@ -1981,29 +1980,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         flush(0, sp_n);
         if (DUAL) flush(1, sb_n);
     }
-    if (wspill && lane() == 0) sm.spilled = 1;
-    __syncthreads();
-    // A part whose candidates overflowed its stage (a row whose tail is most
-    // of the row) also publishes the key range of its primary candidates, so
-    // that the finisher can recognise a tail of equal keys without reading
-    // it; any other part publishes the empty-knowledge range [0, kNoElem].
-    const bool heavy = sm.spilled != 0;
-    if (heavy) {
-        for (uint32_t e = lane(); e < sp_n; e += 64) {
-            const uint32_t key = stg[e].y;
-            pmin = key < pmin ? key : pmin;
-            pmax = key > pmax ? key : pmax;
-        }
-        lds_extremes(&sm.kext[0], pmin, pmax);
-        __syncthreads();
+    // The part also publishes the key range of its stored primary candidates
+    // ([kNoElem, 0] when it has none): the finisher's first digit window, and
+    // a tail of equal keys recognised without reading it.  Staged copies of a
+    // flood key left out above carry a key that is also stored, so they do
+    // not change the range.
+    for (uint32_t e = lane(); e < sp_n; e += 64) {
+        const uint32_t key = stg[e].y;
+        pmin = key < pmin ? key : pmin;
+        pmax = key > pmax ? key : pmax;
     }
+    lds_extremes(&sm.kext[0], pmin, pmax);
+    __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t* counts = kv_counts(p, row);
         counts[2 * part] = sm.cnt[0];
         counts[2 * part + 1] = sm.cnt[1];
         uint32_t* ext = kv_ext(p, row);
-        ext[2 * part] = heavy ? sm.kext[0] : 0u;
-        ext[2 * part + 1] = heavy ? sm.kext[1] : kNoElem;
+        ext[2 * part] = sm.kext[0];
+        ext[2 * part + 1] = sm.kext[1];
     }
 }
 
@@ -2014,24 +2009,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     const uint32_t per_xcd = gridDim.x / 8;
     const uint32_t row = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (row >= static_cast<uint32_t>(p.m_cap)) return;
-    // The live-row count, the row's length and the parts' counts (wave 0,
-    // four parts per lane) are loaded together; counts of parts the row did
-    // not use this call are stale and are dropped below.
+    // The live-row count, the row's length and the parts' counts and key
+    // ranges (wave 0, four parts per lane) are loaded together; entries of
+    // parts the row did not use this call are stale and are dropped below.
     const int32_t nvr = *p.num_valid_rows;
     const int32_t ke_row = p.ke[row];
     uint32_t hkey = 0;
     bool hinted = false;
     if constexpr (HINT) hinted = row_hint(p, row, &hkey);
     const uint32_t* counts = kv_counts(p, row);
-    uint32_t c4[2][4];
+    const uint32_t* exts = kv_ext(p, row);
+    uint32_t c4[2][4], e4[2][4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const uint32_t pp = 4 * lane() + v;
         c4[0][v] = 0;
         c4[1][v] = 0;
+        e4[0][v] = kNoElem;
+        e4[1][v] = 0;
         if (wave() == 0 && pp < static_cast<uint32_t>(p.splits)) {
             c4[0][v] = counts[2 * pp];
             c4[1][v] = counts[2 * pp + 1];
+            e4[0][v] = exts[2 * pp];
+            e4[1][v] = exts[2 * pp + 1];
         }
     }
     const uint32_t m_live = clamp_len(nvr, p.m_cap);
@@ -2048,10 +2048,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     uint32_t* h1 = sm.hist[1];
 
     // Merge the parts (Eq. 27): wave 0 forms the prefix offsets of the
-    // primary and band counts and the largest count of one part; one barrier
-    // publishes them.
+    // primary and band counts, the largest count of one part and the key
+    // range of the primary candidates; one barrier publishes them.
     if (wave() == 0) {
-        uint32_t mxp = 0;
+        uint32_t mxp = 0, kmn = kNoElem, kmx = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            if (4 * lane() + v < Pr) {
+                kmn = e4[0][v] < kmn ? e4[0][v] : kmn;
+                kmx = e4[1][v] > kmx ? e4[1][v] : kmx;
+            }
+        }
+        kmn = wave_min(kmn);
+        kmx = wave_max(kmx);
 #pragma unroll
         for (int kind = 0; kind < 2; ++kind) {
             uint32_t s4 = 0;
@@ -2074,6 +2083,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         mxp = wave_max(mxp);
         if (lane() == 0) {
             sm.part_max = mxp;
+            sm.kext[0] = kmn;
+            sm.kext[1] = kmx;
             sm.out_cnt = 0;
         }
     }
@@ -2092,6 +2103,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     }
     count_route(p, route);
     if (ctot <= static_cast<uint32_t>(kBlock * kRegs)) {
+        const uint32_t klo = sm.kext[0], khi = sm.kext[1];
         // Register slots: when no part holds more than cap = 2^lc candidates
         // of a kind, with nr * cap <= kBlock * kRegs for the nr part ranges in
         // use, range q takes slots [q cap, (q + 1) cap) and a slot finds its
@@ -2150,14 +2162,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
                 src[u] = live[u] ? sv : 0u;
             }
         }
-        refine_regs<kRegs>(
-            [&](int u, uint32_t& i, uint32_t& key) {
-                const uint2 t2 = region[src[u]];
-                i = t2.x;
-                key = t2.y;
-                return live[u];
-            },
-            h1, h0, k, 0u, outp, k, sm);
+        auto ld = [&](int u, uint32_t& i, uint32_t& key) {
+            const uint2 t2 = region[src[u]];
+            i = t2.x;
+            key = t2.y;
+            return live[u];
+        };
+        // the primary candidates' key range is the parts' published one
+        if (route == TOPKF_ROUTE_PRIMARY) refine_regs<kRegs, true>(ld, h1, h0, k, 0u, outp, k, sm, klo, khi);
+        else refine_regs<kRegs>(ld, h1, h0, k, 0u, outp, k, sm);
         return;
     }
     // Large frontier.  When every candidate carries the same key (a constant
