@@ -1765,6 +1765,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         constexpr bool RAW = decltype(raw_c)::value;
         constexpr bool FLOOD = decltype(flood_c)::value;
         return [&](u32x4 b, uint32_t i0) {
+            if constexpr (FLOOD) {
+                // Once this part holds K stored copies of its primary flood
+                // value, a step whose every element carries that bit pattern
+                // would only be left out below: skip it outright.
+                if (full[0] != kNoElem) {
+                    const uint32_t fb = bits_of_key(full[0]);
+                    const bool same = b[0] == fb && b[1] == fb && b[2] == fb && b[3] == fb;
+                    if (__builtin_amdgcn_ballot_w64(!same) == 0) return;
+                }
+            }
             uint32_t key[4];
             bool pp[4], pb[4];
             uint64_t mp[4], mb[4];
