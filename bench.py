@@ -108,8 +108,16 @@ def algorithmic_bytes(ke, n: int, k: int, stride: int, parts: int = 1) -> int:
 
 
 def source_digest() -> str:
+    """Digest of the kernel source's code: its lines with // comments and
+    surrounding blanks removed, empty lines dropped (an edit of comments alone
+    keeps the digest)."""
     src = os.path.join(ROOT, "exact_row_wise_sampled_amd", "csrc", "topkf.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    code = []
+    for line in open(src, encoding="utf-8"):
+        cut = line.split("//", 1)[0].strip()
+        if cut:
+            code.append(cut)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def measured_traffic(config: str):
