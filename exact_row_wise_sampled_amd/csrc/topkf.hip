@@ -1624,10 +1624,11 @@ __device__ __forceinline__ uint32_t segment_chunk(uint32_t L, uint32_t Pr) {
 // contiguous segment, writing the admitted (index, key) pairs into the
 // segment's own range of the row's region (primary candidates upward from
 // the segment start, band candidates T0 < key <= T1 downward from its end)
-// and their two counts.  kvsplit_finish_kernel: one workgroup per row sums
-// the counts (Eq. 27), gathers the candidates into LDS, counts their leading
-// digit and refines.  The kernel boundary makes every part's writes visible
-// to the finisher on any XCD without per-workgroup cache write-back.
+// and their two counts, with the key range of its stored primary candidates.
+// kvsplit_finish_kernel: one workgroup per row sums the counts (Eq. 27) and
+// the key ranges, loads the candidates into registers and refines them in
+// that range.  The kernel boundary makes every part's writes visible to the
+// finisher on any XCD without per-workgroup cache write-back.
 // Workgroups are numbered so that the parts of a row sit on one XCD (the
 // dispatcher deals workgroup ids round-robin over the 8 XCDs), which keeps the
 // replicated view reads in that XCD's L2.
