@@ -1434,9 +1434,16 @@ struct NextRow {
 // row ends its loop.  The draw of ticket M_live - 1 is therefore the last
 // access of the launch to the queue, and that workgroup returns it to zero; no
 // other ordering is needed.  Thread 0 only.
+//
+// The queue serves rows [W, M_live) from the last one down (W = the pool
+// size; the first wave takes rows 0 .. W - 1): in causal prefill a row's
+// length grows with its index, so the longest rows go first and the rows
+// still running when the queue is empty are the shortest.  Returns M_live for
+// no row.
 __device__ __forceinline__ int publish_ticket(const Params& p, uint32_t t, int m_live, Shared& sm) {
     if (t + 1 == static_cast<uint32_t>(m_live)) atomicExch(p.counters, 0u);
-    const int rn = static_cast<int>(gridDim.x + t);
+    const int left = m_live - static_cast<int>(gridDim.x);
+    const int rn = static_cast<int>(t) < left ? m_live - 1 - static_cast<int>(t) : m_live;
     sm.next_row = rn;
     return rn;
 }
