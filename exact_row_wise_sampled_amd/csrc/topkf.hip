@@ -1479,6 +1479,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     WaveFrontier wf{sm.front + wave() * kWaveCap, sliceA + wave() * wsl, 0};
     int route = TOPKF_ROUTE_EXACT_DIRECT;
     bool certified = false;
+    bool done = false;  // refined from the registers loaded at the publish
     uint32_t C = 0;
     uint32_t na = 0, nnv = 0;  // the next row's view
     const float* xn = nullptr;
@@ -1538,9 +1539,59 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                     }
                 });
             nr.looked = on;
-            C = publish_waves(wf, sm);
+            {
+                // Each wave loads its own frontier share into registers as
+                // soon as its scan is done (other waves may still be
+                // scanning) and puts its keys' range next to its size: a
+                // certified row on the primary route refines from these
+                // registers in that range, with no load, reduction or barrier
+                // of its own.
+                uint32_t pidx[kWaveRegs], pkey[kWaveRegs];
+                uint32_t pact = 0;
+                const uint2* reg = sm.front + wave() * kWaveCap;
+                const uint32_t mine = readfirst(wf.n);
+                uint32_t mn = kNoElem, mx = 0;
+#pragma unroll
+                for (int u = 0; u < kWaveRegs; ++u) {
+                    const uint32_t e = lane() + 64 * u;
+                    const bool in = e < mine;
+                    const uint2 v = reg[in ? e : 0u];
+                    pidx[u] = v.x;
+                    pkey[u] = desc_key(v.y);
+                    pact |= in ? 1u << u : 0u;
+                    mn = in && pkey[u] < mn ? pkey[u] : mn;
+                    mx = in && pkey[u] > mx ? pkey[u] : mx;
+                }
+                mn = wave_min(mn);
+                mx = wave_max(mx);
+                if (lane() == 0) {
+                    sm.wext[0][wave()] = mn;
+                    sm.wext[1][wave()] = mx;
+                }
+                clear_hist(h1);
+                C = publish_waves(wf, sm);
+                uint32_t wmax = 0;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) wmax = sm.wcnt[w] > wmax ? sm.wcnt[w] : wmax;
+                if (C >= k && wmax <= static_cast<uint32_t>(kWaveCap)) {
+                    if (hinted) count_route(p, TOPKF_ROUTE_HINTED);
+                    count_route(p, TOPKF_ROUTE_PRIMARY);
+                    const uint4* we = reinterpret_cast<const uint4*>(&sm.wext[0][0]);
+                    const uint4 a = we[0], b = we[1], c = we[2], d = we[3];
+                    const uint32_t lo = min(min(min(a.x, a.y), min(a.z, a.w)), min(min(b.x, b.y), min(b.z, b.w)));
+                    const uint32_t hi = max(max(max(c.x, c.y), max(c.z, c.w)), max(max(d.x, d.y), max(d.z, d.w)));
+                    refine_regs<kWaveRegs, true>(
+                        [&](int u, uint32_t& i, uint32_t& key) {
+                            i = pidx[u];
+                            key = pkey[u];
+                            return ((pact >> u) & 1u) != 0;
+                        },
+                        h1, h0, k, sm.out_cnt, outp, k, sm, lo, hi);
+                    done = true;
+                }
+            }
             route = TOPKF_ROUTE_PRIMARY;
-            if (C < k) {
+            if (!done && C < k) {
                 route = TOPKF_ROUTE_EXACT_UNDERFILL;
                 if (DUAL && T1 > T0) {
                     scan_span<kRowVec>(sp, NoPre{}, [&](u32x4 b, uint32_t i0) {
@@ -1552,23 +1603,25 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                 }
             }
             certified = C >= k;
-            if (hinted) count_route(p, TOPKF_ROUTE_HINTED);
+            if (hinted && !done) count_route(p, TOPKF_ROUTE_HINTED);
         }
     }
-    uint32_t kq = k;
-    if (!certified) {
-        // The no-view plan serves short rows: keep them in registers.
-        kq = exact_route<S == 0>(x, L, k, outp, wf, h0, sm);
-        C = 0;
+    if (!done) {
+        uint32_t kq = k;
+        if (!certified) {
+            // The no-view plan serves short rows: keep them in registers.
+            kq = exact_route<S == 0>(x, L, k, outp, wf, h0, sm);
+            C = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) C += sm.wcnt[w];
+            for (int w = 0; w < kWaves; ++w) C += sm.wcnt[w];
+        }
+        count_route(p, route);
+        bool spill = false;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
+        if (spill) count_route(p, TOPKF_ROUTE_SPILL);
+        finish_waves(C, sliceA, wsl, sliceB, sliceA, h1, h0, kq, outp, k, sm);
     }
-    count_route(p, route);
-    bool spill = false;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) spill |= sm.wcnt[w] > static_cast<uint32_t>(kWaveCap);
-    if (spill) count_route(p, TOPKF_ROUTE_SPILL);
-    finish_waves(C, sliceA, wsl, sliceB, sliceA, h1, h0, kq, outp, k, sm);
     clear_hist(h0);  // for the next row's view (made visible by the caller's barrier)
     // The next row's first batch of view samples goes out now, so that it has
     // arrived when that row starts, and the sampled lines are still cached
