@@ -2780,7 +2780,8 @@ void plan_sizes(const topkf_plan& pl, int64_t m_cap, int64_t n, size_t* cb, size
         // two (index, key) slices per worker: wave spills, contiguous frontier
         *wb = static_cast<size_t>(pl.workers) * per_owner;
     } else {
-        // per row: part ranges and contiguous frontier, then two counts per part
+        // per row: part ranges and contiguous frontier, then four words per part
+        // (the two candidate counts and the smallest and largest stored key)
         *wb = static_cast<size_t>(m_cap) *
               (per_owner + 4 * static_cast<size_t>(pl.splits) * sizeof(uint32_t));
     }
