@@ -2186,7 +2186,30 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         while (lc > 0 && (nr << lc) > static_cast<uint32_t>(kBlock * kRegs)) --lc;
         uint32_t src[kRegs];
         bool live[kRegs];
-        if (sm.part_max <= (1u << lc)) {
+        if (sm.part_max <= (1u << lc) && route == TOPKF_ROUTE_PRIMARY) {
+            // Slot gq = tid + kBlock u: with kBlock = 2^9, its range is
+            // (kBlock u) >> lc when lc >= 9 (the same for the whole block)
+            // and (u << (9 - lc)) + (tid >> lc) otherwise, its position in
+            // the range (kBlock u) & (cap - 1) + tid or tid & (cap - 1):
+            // a per-thread part set once and a uniform part per slot.
+            static_assert(kBlock == 512, "the slot split below assumes kBlock = 2^9");
+            const uint32_t cap = 1u << lc;
+            const bool wide = lc >= 9;
+            const uint32_t tq = wide ? 0u : threadIdx.x >> lc;
+            const uint32_t jt = wide ? threadIdx.x : threadIdx.x & (cap - 1u);
+            const uint32_t tbase = tq * chunk + jt;
+#pragma unroll
+            for (int u = 0; u < kRegs; ++u) {
+                const uint32_t qs = wide ? (static_cast<uint32_t>(kBlock) * u) >> lc
+                                         : static_cast<uint32_t>(u) << (9 - lc);
+                const uint32_t js = wide ? (static_cast<uint32_t>(kBlock) * u) & (cap - 1u) : 0u;
+                const uint32_t q = qs + tq;
+                const uint32_t* o = sm.offs[0] + (q < Pr ? q : 0u);
+                const uint32_t n = o[1] - o[0];
+                live[u] = (q < Pr) & (js + jt < n);
+                src[u] = live[u] ? qs * chunk + js + tbase : 0u;
+            }
+        } else if (sm.part_max <= (1u << lc)) {
             // every LDS read unconditional, so that they issue together
 #pragma unroll
             for (int u = 0; u < kRegs; ++u) {
