@@ -2738,17 +2738,20 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
     // Mapping (Sec. 5.5).  With at least a full pool of rows, persistent
     // workers.  With a quarter of the pool or fewer, one workgroup per row
     // unless the rows are long: KV-split pays for its second launch and its
-    // replicated views only from N >= 2048 * max(M, 64) columns (measured:
-    // M = 64 gains 9 % at N = 128K, M = 128 breaks even at 256K, and every
-    // M up to 64 loses at 64K).  In between, KV-split: one workgroup per row
-    // is about 20 % faster on i.i.d. rows but a row whose admitted tail is
-    // most of the row (constant or heavily tied) then streams its whole
-    // frontier through one workgroup, 3-4 times slower on the adversarial
-    // mix, where the split spreads it over the parts.
+    // replicated views from N >= 1024 * max(M, 64) columns (measured on
+    // MI355X, ke ~ U[N/2, N], K = 2048, us per call, one workgroup per row
+    // against the best split: 4 x 32K 13.0 / 15.2, 4 x 64K 18.3 / 15.9,
+    // 64 x 64K 18.7 / 16.8, 128 x 64K 19.5 / 20.6, 128 x 128K 28.1 / 25.8,
+    // 128 x 256K 42.8 / 36.3).  In between, KV-split: one workgroup per row
+    // is up to 13 % faster on some i.i.d. shapes (256 x 128K: 32.1 / 36.4;
+    // 384 x 128K: 52.9 / 51.0) but a row whose admitted tail is most of the
+    // row (constant or heavily tied) then streams its whole frontier
+    // through one workgroup, 3-4 times slower on the adversarial mix, where
+    // the split spreads it over the parts.
     bool kv = false;
     if (r.stride != 0 && m_cap < pool) {
         if (4 * rows > pool) kv = true;
-        else kv = n >= 2048 * (rows > 64 ? rows : 64);
+        else kv = n >= 1024 * (rows > 64 ? rows : 64);
     }
     if (!kv) {
         r.family = TOPKF_FAMILY_PERSISTENT;
@@ -2762,15 +2765,16 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         // round, and 2K is 4 % faster than 1.75K (2.25K no faster).
         r.primary_quarters = 8;
     } else {
-        // Parts per row: enough to fill the pool twice over, but no segment
-        // shorter than 16K columns (shorter segments lose more to the
-        // replicated view than they gain in span).  With ragged rows a part
-        // streams its segment at the rate one workgroup sustains, so the
-        // longest rows need several parts even when that overfills the pool
-        // and later parts wait for a slot (measured on 256 rows of up to 256K
-        // columns: 2 parts 95.7 us, 4 parts 80.0 us, 8 parts 81.4 us, 16 parts
-        // 89.0 us); decode and few-long-row shapes reach the segment floor
-        // first and are unchanged.
+        // Parts per row: half the pool's slots over the rows (every part on
+        // a CU of its own), at least 4 (up to 2 pool / M) so that the longest
+        // rows of a ragged batch are split, and no segment shorter than 16K
+        // columns (shorter segments lose more to the replicated view than
+        // they gain in span).  Measured (us per call at 1 / 2 / 4 / 8 / 16
+        // parts): 64 x 128K 34.0 / 25.0 / 20.6 / 21.4, 32 x 128K 33.5 / 24.5 /
+        // 19.8 / 18.7, 128 x 128K 35.0 / 26.6 / 25.8 / 31.0, 64 x 512K 81.5 /
+        // 52.0 / 38.1 / 41.0 / 46.1, 256 x 256K 60.8 / 58.8 / 58.6 / 61.6 /
+        // 70.7; few long rows reach the segment floor first (4 x 512K: 32
+        // parts 21.8 us).
         r.family = TOPKF_FAMILY_KVSPLIT;
         // Primary boundary only, at K~ = 2K.  Collecting the band in the
         // fused pass costs every part a second classification of every
@@ -2782,7 +2786,9 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         // the exact coarse route, so the result stays exact.
         r.dual = 0;
         r.primary_quarters = 8;
-        int64_t P = (2 * pool + rows - 1) / rows;
+        const int64_t half_pool = (pool + 2 * rows - 1) / (2 * rows);
+        const int64_t spread = (2 * pool + rows - 1) / rows;
+        int64_t P = half_pool > (spread < 4 ? spread : 4) ? half_pool : (spread < 4 ? spread : 4);
         int64_t pmax = (n + r.min_segment - 1) / r.min_segment;
         if (pmax > kMaxSplits) pmax = kMaxSplits;
         if (P > pmax) P = pmax;

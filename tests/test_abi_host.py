@@ -62,7 +62,7 @@ def test_planner_maps_workload_shapes():
     assert prefill.workers == 2 * cus and prefill.dual == 1
     decode = topkf.plan_for(64, 131072, cus)
     assert decode.family == topkf.FAMILY_KVSPLIT and decode.stride == 128
-    assert decode.splits * 64 >= 2 * cus
+    assert decode.splits * 64 >= cus
     long_ = topkf.plan_for(4, 524288, cus)
     assert long_.family == topkf.FAMILY_KVSPLIT
     assert long_.splits <= 524288 // long_.min_segment
@@ -70,18 +70,26 @@ def test_planner_maps_workload_shapes():
     assert mid.stride == 128 and mid.family == topkf.FAMILY_PERSISTENT
     assert topkf.plan_for(1024, 12288, cus).stride == 128
     assert topkf.plan_for(1024, 8192, cus).stride == 0
-    # Few rows: one workgroup per row unless the rows are long.
-    for m, n, fam in ((64, 65536, topkf.FAMILY_PERSISTENT), (4, 65536, topkf.FAMILY_PERSISTENT),
-                      (4, 131072, topkf.FAMILY_KVSPLIT), (128, 131072, topkf.FAMILY_PERSISTENT),
+    # Few rows: one workgroup per row unless the rows are long
+    # (N >= 1024 * max(M, 64)).
+    for m, n, fam in ((64, 65536, topkf.FAMILY_KVSPLIT), (4, 65536, topkf.FAMILY_KVSPLIT),
+                      (4, 32768, topkf.FAMILY_PERSISTENT), (128, 65536, topkf.FAMILY_PERSISTENT),
+                      (64, 32768, topkf.FAMILY_PERSISTENT),
+                      (4, 131072, topkf.FAMILY_KVSPLIT), (128, 131072, topkf.FAMILY_KVSPLIT),
                       (128, 262144, topkf.FAMILY_KVSPLIT), (256, 65536, topkf.FAMILY_KVSPLIT),
                       (256, 262144, topkf.FAMILY_KVSPLIT), (512, 262144, topkf.FAMILY_PERSISTENT)):
         pl = topkf.plan_for(m, n, cus)
         assert pl.family == fam, (m, n, pl)
         if fam == topkf.FAMILY_PERSISTENT:
             assert pl.workers == min(m, 2 * cus)
-    assert long_.splits == 32 and decode.splits == 8
-    # ragged mid-size rows: parts for twice the pool, the longest rows split 4 ways
+    assert long_.splits == 32 and decode.splits == 4
+    # parts: half the pool over the rows, at least min(4, 2 pool / M), within
+    # the 16K-column segment floor
+    assert topkf.plan_for(32, 131072, cus).splits == 8
+    assert topkf.plan_for(128, 262144, cus).splits == 4
     assert topkf.plan_for(256, 262144, cus).splits == 4
+    assert topkf.plan_for(384, 131072, cus).splits == 3
+    assert topkf.plan_for(4, 65536, cus).splits == 4
     assert decode.dual == 0 and decode.primary_quarters == 8
     assert prefill.primary_quarters == 8 and prefill.band_quarters == 10
 
