@@ -1483,6 +1483,7 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     uint32_t C = 0;
     uint32_t na = 0, nnv = 0;  // the next row's view
     const float* xn = nullptr;
+    uint32_t vnext0 = kNoElem;  // its first sample per thread
     if constexpr (S > 0) {
         uint32_t a;
         const uint32_t nv = view_size<S>(row, L, &a);
@@ -1539,6 +1540,11 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                     }
                 });
             nr.looked = on;
+            // The next row's first view sample per thread goes out now, ahead
+            // of this row's refinement, so that it has arrived when that row
+            // starts counting its view (the rest of a longer view follows at
+            // the end of this row).
+            if (on) vnext0 = threadIdx.x < nnv ? __float_as_uint(xn[na + threadIdx.x * S]) : kNoElem;
             {
                 // Each wave loads its own frontier share into registers as
                 // soon as its scan is done (other waves may still be
@@ -1627,7 +1633,14 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
     // arrived when that row starts, and the sampled lines are still cached
     // when its scan reads them.
     if constexpr (S > 0) {
-        if (nr.looked) view_batch(xn, na, nnv, S, 0u, nr.vb);
+        if (nr.looked) {
+            nr.vb[0] = vnext0;
+#pragma unroll
+            for (int u = 1; u < kSampleVec; ++u) {
+                const uint32_t j = u * kBlock + threadIdx.x;
+                nr.vb[u] = j < nnv ? __float_as_uint(xn[na + j * S]) : kNoElem;
+            }
+        }
     }
     return nr;
 }
