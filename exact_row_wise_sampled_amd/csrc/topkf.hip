@@ -581,18 +581,18 @@ __device__ __forceinline__ void block_find(const uint32_t* hist, const uint32_t 
     __syncthreads();
     uint32_t all;
     const uint32_t excl = waves_below(sm.wsum[0], &all) + incl - s;
+    // The bin within the thread's four: the number of partial sums below
+    // the target, with no branch and no per-bin constant (such constants get
+    // spilled, and the reload's wait would also wait for every load the
+    // thread has in flight).
+    const uint32_t a1 = excl + v.x, a2 = a1 + v.y, a3 = a2 + v.z;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
         if (excl < t[i] && t[i] <= excl + s) {
-            uint32_t acc = excl, b = 4 * tid, c = v.x;
-            if (acc + v.x < t[i]) {
-                acc += v.x; b += 1; c = v.y;
-                if (acc + v.y < t[i]) {
-                    acc += v.y; b += 1; c = v.z;
-                    if (acc + v.z < t[i]) { acc += v.z; b += 1; c = v.w; }
-                }
-            }
-            sm.res[2 * i] = b;
+            const uint32_t st = (a1 < t[i] ? 1u : 0u) + (a2 < t[i] ? 1u : 0u) + (a3 < t[i] ? 1u : 0u);
+            const uint32_t acc = st == 0 ? excl : st == 1 ? a1 : st == 2 ? a2 : a3;
+            const uint32_t c = st == 0 ? v.x : st == 1 ? v.y : st == 2 ? v.z : v.w;
+            sm.res[2 * i] = 4 * tid + st;
             sm.res[2 * i + 1] = acc;
             sm.rcnt[i] = c;
         }
