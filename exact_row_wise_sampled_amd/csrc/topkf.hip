@@ -1544,6 +1544,10 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
             // of this row's refinement, so that it has arrived when that row
             // starts counting its view (the rest of a longer view follows at
             // the end of this row).
+            // Nothing this wave issued is still in flight here; the explicit
+            // wait says so, and without it the compiler waits for this load
+            // as soon as a register of the scan's ring is reused.
+            __builtin_amdgcn_s_waitcnt(0);
             if (on) vnext0 = threadIdx.x < nnv ? __float_as_uint(xn[na + threadIdx.x * S]) : kNoElem;
             {
                 // Each wave loads its own frontier share into registers as
