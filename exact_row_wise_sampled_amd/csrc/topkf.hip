@@ -1610,6 +1610,11 @@ __device__ __forceinline__ NextRow select_row(const Params& p, int row, uint32_t
                     __syncthreads();
                     C = publish_waves(wf, sm);
                     if (C >= k) route = TOPKF_ROUTE_BAND;
+                    // Drained here, so that no load of this pass is still
+                    // counted where the code paths meet again: otherwise the
+                    // compiler makes the primary route's refinement wait for
+                    // the next row's view load (issued above) before it starts.
+                    __builtin_amdgcn_s_waitcnt(0);
                 }
             }
             certified = C >= k;

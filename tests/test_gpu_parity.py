@@ -38,6 +38,25 @@ def test_workload_prefill_auto_plan():
     note("routes %s" % st)
 
 
+@pytest.mark.parametrize("m,n", [(64, 65536), (4, 65536), (128, 131072), (32, 131072)])
+def test_planner_kvsplit_shapes_auto_plan(m, n):
+    """Shapes whose automatic plan is KV-split with 4 or 8 parts (one part
+    per CU): ragged decode-model rows with ke ~ U[N/2, N], the first row cut
+    to a length of 3 mod 4 and the last to exactly K + 1 (both shorter than
+    the generated length, so every valid score is a generated one)."""
+    t = topkf()
+    w = W.decode(seed=50 + m, m=m, n=n, lo=n // 2)
+    ke = w.ke.copy()
+    ke[0] = (int(ke[0]) // 4) * 4 - 1
+    ke[-1] = w.k + 1
+    plan = t.plan_for(m, n, 256)
+    assert plan.family == t.FAMILY_KVSPLIT, plan
+    note("planner KV shape M=%d N=%d splits=%d" % (m, n, plan.splits))
+    out, st, _ = run_topk(w.x, ke, w.k, stats=True)
+    assert_exact(out, w.x, ke, w.k)
+    note("routes %s" % st)
+
+
 # -------------------------------------------------------- forced mappings
 
 def plans():
