@@ -2788,7 +2788,7 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         r.primary_quarters = 8;
     } else {
         // Parts per row: half the pool's slots over the rows (every part on
-        // a CU of its own), at least 4 (up to 2 pool / M) so that the longest
+        // a CU of its own), at least 4 (at most 2 pool / M) so that the longest
         // rows of a ragged batch are split, and no segment shorter than 16K
         // columns (shorter segments lose more to the replicated view than
         // they gain in span).  Measured (us per call at 1 / 2 / 4 / 8 / 16
@@ -2808,7 +2808,10 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
         // the exact coarse route, so the result stays exact.
         r.dual = 0;
         r.primary_quarters = 8;
-        const int64_t half_pool = (pool + 2 * rows - 1) / (2 * rows);
+        // rounded down: a grid just above the CU count leaves some CUs two
+        // parts and the launch waits for them (decode at 3 / 4 / 5 / 6 parts,
+        // 192 / 256 / 320 / 384 workgroups: 22.2 / 20.4 / 24.4 / 23.9 us)
+        const int64_t half_pool = pool / (2 * rows) > 1 ? pool / (2 * rows) : 1;
         const int64_t spread = (2 * pool + rows - 1) / rows;
         int64_t P = half_pool > (spread < 4 ? spread : 4) ? half_pool : (spread < 4 ? spread : 4);
         int64_t pmax = (n + r.min_segment - 1) / r.min_segment;

@@ -90,6 +90,9 @@ def test_planner_maps_workload_shapes():
     assert topkf.plan_for(256, 262144, cus).splits == 4
     assert topkf.plan_for(384, 131072, cus).splits == 3
     assert topkf.plan_for(4, 65536, cus).splits == 4
+    # rounded down, so that the grid does not just exceed the CU count
+    assert topkf.plan_for(48, 131072, cus).splits == 5
+    assert topkf.plan_for(40, 131072, cus).splits == 6
     assert decode.dual == 0 and decode.primary_quarters == 8
     assert prefill.primary_quarters == 8 and prefill.band_quarters == 10
 
