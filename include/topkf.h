@@ -40,7 +40,7 @@ extern "C" {
 typedef enum {
     TOPKF_OK = 0,
     TOPKF_EINVAL = 1,       /* a host-checkable argument is invalid */
-    TOPKF_EUNSUPPORTED = 2, /* valid request this build does not serve */
+    TOPKF_EUNSUPPORTED = 2, /* valid request the library does not serve */
     TOPKF_EWORKSPACE = 3,   /* counters or workspace smaller than required */
     TOPKF_EHIP = 4          /* a HIP runtime call or kernel launch failed */
 } topkf_status;
