@@ -38,10 +38,11 @@ def test_workload_prefill_auto_plan():
     note("routes %s" % st)
 
 
-@pytest.mark.parametrize("m,n", [(64, 65536), (4, 65536), (128, 131072), (32, 131072)])
+@pytest.mark.parametrize("m,n", [(64, 65536), (4, 65536), (128, 131072), (32, 131072),
+                                 (48, 131072), (40, 131072)])
 def test_planner_kvsplit_shapes_auto_plan(m, n):
-    """Shapes whose automatic plan is KV-split with 4 or 8 parts (one part
-    per CU): ragged decode-model rows with ke ~ U[N/2, N], the first row cut
+    """Shapes whose automatic plan is KV-split with 4, 5, 6 or 8 parts (about
+    one part per CU): ragged decode-model rows with ke ~ U[N/2, N], the first row cut
     to a length of 3 mod 4 and the last to exactly K + 1 (both shorter than
     the generated length, so every valid score is a generated one)."""
     t = topkf()
