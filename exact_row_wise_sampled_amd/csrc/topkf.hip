@@ -2741,11 +2741,14 @@ topkf_status make_plan(int64_t m_cap, int64_t n, int32_t cus, int32_t occupancy,
     topkf_plan r{};
     // View policy (Sec. 5.5: s = 64 and s = 128 compile-time policies;
     // Sec. 6.4 Fig. 12: sampling pays off for wide rows, exact localization
-    // for short ones).  Measured on MI355X at K = 2048 over M = 64..4096:
-    // the exact route wins below 8K columns, the two are even at 8K, the
-    // view wins from 12K on, and s = 128 is as fast as or faster than s = 64
-    // from 12K up (up to 12 % at 128K), so s = 64 is left to explicit plans.
-    r.stride = n < 12288 ? 0 : 128;
+    // for short ones).  Measured on MI355X at K = 2048 over M = 64..4096
+    // (ke ~ U[N/2, N]): the exact route keeps a row of up to 8K scores in
+    // registers and wins below 8K columns, the two are within 5 % at 8K, and
+    // past 8K (the exact route then reads the row twice) the view wins by
+    // 25-40 % (10K: 11.5 / 15.9 us at M = 64, 89.9 / 119.9 us at M = 4096);
+    // s = 128 is as fast as or faster than s = 64 (up to 12 % at 128K), so
+    // s = 64 is left to explicit plans.
+    r.stride = n <= 8192 ? 0 : 128;
     r.dual = r.stride ? 1 : 0;
     r.min_segment = 16384;
     // Secondary target K~1 = 2.5K (Sec. 4.6 treats K~ and K~1 as efficiency

@@ -69,6 +69,7 @@ def test_planner_maps_workload_shapes():
     mid = topkf.plan_for(1024, 32768, cus)
     assert mid.stride == 128 and mid.family == topkf.FAMILY_PERSISTENT
     assert topkf.plan_for(1024, 12288, cus).stride == 128
+    assert topkf.plan_for(1024, 8193, cus).stride == 128
     assert topkf.plan_for(1024, 8192, cus).stride == 0
     # Few rows: one workgroup per row unless the rows are long
     # (N >= 1024 * max(M, 64)).

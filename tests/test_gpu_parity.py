@@ -58,6 +58,20 @@ def test_planner_kvsplit_shapes_auto_plan(m, n):
     note("routes %s" % st)
 
 
+@pytest.mark.parametrize("m,n", [(64, 10240), (1024, 8193)])
+def test_planner_view_just_past_register_rows(m, n):
+    """Rows just past the 8192 scores the exact route keeps in registers take
+    the view on the automatic plan."""
+    t = topkf()
+    w = W.decode(seed=70 + m, m=m, n=n, lo=n // 2)
+    plan = t.plan_for(m, n, 256)
+    assert plan.family == t.FAMILY_PERSISTENT and plan.stride == 128, plan
+    note("planner view shape M=%d N=%d" % (m, n))
+    out, st, _ = run_topk(w.x, w.ke, w.k, stats=True)
+    assert_exact(out, w.x, w.ke, w.k)
+    note("routes %s" % st)
+
+
 # -------------------------------------------------------- forced mappings
 
 def plans():
